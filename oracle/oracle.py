@@ -1,0 +1,183 @@
+"""fp64 CPU oracle for MLA absorb-path decode -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this module.  The product path (the HIP library and its
+binding) never does, and this module imports nothing from it.
+
+Two independent implementations live here:
+
+* ``attend`` / ``lse_merge`` wrap ``mla_oracle.c``: the absorb path, plain
+  loops in double precision (see that file's header for the passages each step
+  follows).
+* ``expand_attention`` is the *expand* path in NumPy float64: per-head keys and
+  values are rebuilt from the latent with W_UK and W_UV and an ordinary
+  multi-head attention with 192-wide queries/keys and 128-wide values is run
+  ("MLA inference: two computation paths and FlashMLA", section "Two
+  equivalent paths", path one).  The handbook shows both paths give the same
+  output; tests use that equivalence to pin the absorb oracle.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "mla_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+Q_BF16, Q_F64 = 0, 1
+KV_BF16, KV_E4M3FN = 0, 1
+_STATUS = {0: "ok", -1: "bad argument", -2: "block table entry outside the cache",
+           -3: "seqlen outside [s_q, max_blocks * page_size]", -4: "out of memory"}
+
+
+class _Shape(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_int32) for name in (
+        "batch", "seqlen_q", "num_heads", "d_latent", "d_rope", "page_size", "num_pages",
+        "max_blocks", "causal", "q_dtype", "kv_dtype")] + [("softmax_scale", ctypes.c_float)]
+
+
+def build(force: bool = False) -> str:
+    """Compile mla_oracle.c with gcc (-O2, OpenMP, no fast-math) into liboracle.so."""
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
+                               "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        lib = ctypes.CDLL(build())
+        lib.oracle_bf16_to_f64.restype = ctypes.c_double
+        lib.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
+        lib.oracle_e4m3fn_to_f64.restype = ctypes.c_double
+        lib.oracle_e4m3fn_to_f64.argtypes = [ctypes.c_uint8]
+        lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_mla_attend.restype = ctypes.c_int
+        lib.oracle_mla_attend.argtypes = [ctypes.POINTER(_Shape)] + [ctypes.c_void_p] * 8 + [ctypes.c_int64] + \
+            [ctypes.c_void_p] * 2
+        lib.oracle_lse_merge.restype = ctypes.c_int
+        lib.oracle_lse_merge.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32] + [ctypes.c_void_p] * 4
+        _lib = lib
+    return _lib
+
+
+def num_threads() -> int:
+    """Threads the oracle's OpenMP loops use (OMP_NUM_THREADS, else all cores)."""
+    return int(_load().oracle_num_threads())
+
+
+def bf16_to_f64(bits: int) -> float:
+    return float(_load().oracle_bf16_to_f64(int(bits)))
+
+
+def e4m3fn_to_f64(code: int) -> float:
+    return float(_load().oracle_e4m3fn_to_f64(int(code)))
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def attend(q, cache, block_table, seqlens, *, softmax_scale, causal=False, kv_scale=None,
+           d_rope=64, t_begin=None, t_end=None, rows=None):
+    """Absorb-path attention in fp64 over a paged latent cache.
+
+    q:           uint16 bf16 bits or float64, [B, s_q, H, d_latent + d_rope]
+    cache:       uint16 bf16 bits or uint8 E4M3FN codes, [P, page, d_latent + d_rope]
+    kv_scale:    float32 [P, page] for an E4M3FN cache, else None
+    block_table: int32 [B, max_blocks]; seqlens: int32 [B] (counting the new tokens)
+    t_begin/t_end: optional int32 [B] token window (split mode); rows: optional flat row ids
+
+    Returns (out float64 [nrows, d_latent], lse float64 [nrows]); without ``rows``
+    they are reshaped to [B, s_q, H, d_latent] and [B, s_q, H].
+    """
+    lib = _load()
+    q = np.ascontiguousarray(q)
+    cache = np.ascontiguousarray(cache)
+    block_table = np.ascontiguousarray(block_table, dtype=np.int32)
+    seqlens = np.ascontiguousarray(seqlens, dtype=np.int32)
+    B, s_q, H, D = q.shape
+    P, page, Dc = cache.shape
+    if Dc != D:
+        raise ValueError(f"query width {D} != cache row width {Dc}")
+    if q.dtype == np.float64:
+        q_dtype = Q_F64
+    elif q.dtype == np.uint16:
+        q_dtype = Q_BF16
+    else:
+        raise TypeError("q must be uint16 (bf16 bits) or float64")
+    if cache.dtype == np.uint16:
+        kv_dtype = KV_BF16
+    elif cache.dtype == np.uint8:
+        kv_dtype = KV_E4M3FN
+        if kv_scale is None:
+            raise ValueError("an E4M3FN cache needs kv_scale")
+        kv_scale = np.ascontiguousarray(kv_scale, dtype=np.float32)
+        if kv_scale.shape != (P, page):
+            raise ValueError("kv_scale must be [P, page]")
+    else:
+        raise TypeError("cache must be uint16 (bf16 bits) or uint8 (E4M3FN codes)")
+    shape = _Shape(B, s_q, H, D - d_rope, d_rope, page, P, block_table.shape[1], int(bool(causal)), q_dtype,
+                   kv_dtype, float(np.float32(softmax_scale)))
+    tb = None if t_begin is None else np.ascontiguousarray(t_begin, dtype=np.int32)
+    te = None if t_end is None else np.ascontiguousarray(t_end, dtype=np.int32)
+    if rows is None:
+        nrows = B * s_q * H
+        rows_arr = None
+    else:
+        rows_arr = np.ascontiguousarray(rows, dtype=np.int64)
+        nrows = rows_arr.shape[0]
+    out = np.empty((nrows, D - d_rope), dtype=np.float64)
+    lse = np.empty((nrows,), dtype=np.float64)
+    st = lib.oracle_mla_attend(ctypes.byref(shape), _ptr(q), _ptr(cache), _ptr(kv_scale), _ptr(block_table),
+                               _ptr(seqlens), _ptr(tb), _ptr(te), _ptr(rows_arr), nrows, _ptr(out), _ptr(lse))
+    if st != 0:
+        raise ValueError(f"oracle_mla_attend: {_STATUS.get(st, st)}")
+    if rows is None:
+        return out.reshape(B, s_q, H, D - d_rope), lse.reshape(B, s_q, H)
+    return out, lse
+
+
+def lse_merge(out_parts, lse_parts):
+    """Merge partial (out_j, lse_j) over disjoint windows: out_parts [J, rows, dv], lse_parts [J, rows]."""
+    out_parts = np.ascontiguousarray(out_parts, dtype=np.float64)
+    lse_parts = np.ascontiguousarray(lse_parts, dtype=np.float64)
+    J, R, dv = out_parts.shape
+    out = np.empty((R, dv), dtype=np.float64)
+    lse = np.empty((R,), dtype=np.float64)
+    st = _load().oracle_lse_merge(J, R, dv, _ptr(out_parts), _ptr(lse_parts), _ptr(out), _ptr(lse))
+    if st != 0:
+        raise ValueError(f"oracle_lse_merge: {_STATUS.get(st, st)}")
+    return out, lse
+
+
+def expand_attention(q_nope, q_rope, w_uk, w_uv, latent, k_rope, softmax_scale, query_pos, key_pos):
+    """Expand path (path one) in float64, for one request.
+
+    q_nope [Tq, H, dn], q_rope [Tq, H, dr]; w_uk, w_uv [H, dn|dv, d_latent] (k^N = W_UK[h] c);
+    latent [Tk, d_latent], k_rope [Tk, dr]; query_pos [Tq] and key_pos [Tk] are absolute
+    positions: query at position p sees keys at positions <= p.
+    Returns (out [Tq, H, dv], lse [Tq, H]).
+    """
+    latent = np.asarray(latent, dtype=np.float64)
+    k_nope = np.einsum("hnc,tc->htn", w_uk, latent)          # per-head keys rebuilt from the latent
+    v = np.einsum("hvc,tc->htv", w_uv, latent)               # per-head values rebuilt from the latent
+    logits = (np.einsum("qhn,htn->hqt", q_nope, k_nope) + np.einsum("qhr,tr->hqt", q_rope, k_rope)) * softmax_scale
+    visible = np.asarray(key_pos)[None, :] <= np.asarray(query_pos)[:, None]   # [Tq, Tk]
+    logits = np.where(visible[None], logits, -np.inf)
+    mx = logits.max(axis=-1, keepdims=True)
+    w = np.exp(logits - mx)
+    z = w.sum(axis=-1, keepdims=True)
+    out = np.einsum("hqt,htv->qhv", w / z, v)
+    lse = (mx + np.log(z))[..., 0].T                          # [Tq, H]
+    return out, lse

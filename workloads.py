@@ -1,0 +1,203 @@
+"""Seeded synthetic inputs for MLA absorb-path decode.
+
+This module only draws inputs: random numbers, rounding to the stored formats,
+block tables and NaN poison.  It contains none of the attention arithmetic, and
+both the HIP path's tests/benchmark and the fp64 oracle read what it produces.
+
+Shapes follow DeepSeek-V3's MLA (128 heads, a 512-wide latent plus a 64-wide
+RoPE key per cached token, so 576 numbers per token; pages of 64 tokens), as
+the handbook page "MLA inference: two computation paths and FlashMLA" gives
+them in "Which is faster" and in its FlashMLA paragraph.
+
+Recipe (fixed so any run can be reproduced):
+  * RNG: numpy ``default_rng(seed)`` (PCG64); draw order: seqlens (ragged only)
+    -> page permutation -> q~ -> cache latent -> cache RoPE part.
+  * Values are drawn in float32 and stored as bf16 with round-to-nearest-even;
+    the FP8 cache stores OCP E4M3FN codes of x / s_t with a per-token scale
+    s_t = amax_t / 448 over all 576 numbers of the token (1 when amax is 0).
+  * Cache rows beyond a request's length in its last page, and every page no
+    request references, are filled with NaN: results must not depend on them.
+  * Block-table entries past a request's last page are -1.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional, Sequence
+
+import numpy as np
+
+D_LATENT = 512
+D_ROPE = 64
+D_QK = D_LATENT + D_ROPE
+PAGE = 64
+SOFTMAX_SCALE = np.float32(1.0 / math.sqrt(128 + 64))   # 1/sqrt(d_nope + d_rope)
+
+BF16_NAN = np.uint16(0x7FC0)
+E4M3FN_NAN = np.uint8(0x7F)
+E4M3FN_MAX = 448.0
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bf16 (nearest, ties to even); returns the 16-bit patterns."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    rounded = (u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))) >> np.uint32(16)
+    out = rounded.astype(np.uint16)
+    nan = np.isnan(x)
+    if nan.any():
+        out[nan] = BF16_NAN
+    return out
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def f32_to_e4m3fn(x: np.ndarray) -> np.ndarray:
+    """Encode float32 to OCP E4M3FN codes, round-to-nearest-even, saturating at +-448.
+
+    Uses PyTorch's float8_e4m3fn cast on values already clipped to the finite range.
+    """
+    import torch
+    clipped = np.clip(np.asarray(x, dtype=np.float32), -E4M3FN_MAX, E4M3FN_MAX)
+    return torch.from_numpy(np.ascontiguousarray(clipped)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+@dataclasses.dataclass
+class Workload:
+    name: str
+    q: np.ndarray               # uint16 bf16 bits [B, s_q, H, 576]
+    cache: np.ndarray           # uint16 bf16 bits or uint8 E4M3FN codes [P, 64, 576]
+    kv_scale: Optional[np.ndarray]  # float32 [P, 64] (FP8 only)
+    block_table: np.ndarray     # int32 [B, max_blocks]
+    seqlens: np.ndarray         # int32 [B]
+    s_q: int
+    num_heads: int
+    causal: bool
+    softmax_scale: np.float32 = SOFTMAX_SCALE
+
+    @property
+    def batch(self) -> int:
+        return int(self.seqlens.shape[0])
+
+    @property
+    def num_pages(self) -> int:
+        return int(self.cache.shape[0])
+
+    @property
+    def kv_dtype(self) -> str:
+        return "fp8_e4m3fn" if self.cache.dtype == np.uint8 else "bf16"
+
+
+def _normal_f32(rng: np.random.Generator, shape, chunk_rows: int = 1 << 20) -> np.ndarray:
+    """standard_normal in float32, drawn in row chunks (same stream as one draw) to bound memory."""
+    shape = tuple(shape)
+    out = np.empty(shape, dtype=np.float32)
+    flat = out.reshape(shape[0], -1)
+    for r0 in range(0, shape[0], chunk_rows):
+        r1 = min(shape[0], r0 + chunk_rows)
+        flat[r0:r1] = rng.standard_normal((r1 - r0, flat.shape[1]), dtype=np.float32)
+    return out
+
+
+def make_workload(name: str, *, batch: int, num_heads: int, seqlens: Sequence[int] | np.ndarray, s_q: int = 1,
+                  causal: bool = False, seed: int = 0, latent_std: float = 1.0, q_std: float = 1.0,
+                  rope_std: float = 1.0, kv_dtype: str = "bf16", permute_pages: bool = True,
+                  spare_pages: int = 0, max_blocks: Optional[int] = None, poison: bool = True,
+                  rng: Optional[np.random.Generator] = None) -> Workload:
+    """Draw one decode batch.  ``seqlens`` counts the new tokens (each >= s_q)."""
+    rng = np.random.default_rng(seed) if rng is None else rng
+    seqlens = np.asarray(seqlens, dtype=np.int32)
+    assert seqlens.shape == (batch,) and (seqlens >= s_q).all()
+    npages = (seqlens.astype(np.int64) + PAGE - 1) // PAGE
+    used = int(npages.sum())
+    P = used + spare_pages
+    mb = int(npages.max()) if max_blocks is None else max_blocks
+    assert mb >= npages.max()
+
+    perm = rng.permutation(P).astype(np.int32) if permute_pages else np.arange(P, dtype=np.int32)
+    block_table = np.full((batch, mb), -1, dtype=np.int32)
+    off = 0
+    for b in range(batch):
+        block_table[b, :npages[b]] = perm[off:off + npages[b]]
+        off += int(npages[b])
+
+    q = _normal_f32(rng, (batch, s_q, num_heads, D_QK))
+    if q_std != 1.0:
+        q *= np.float32(q_std)
+    latent = _normal_f32(rng, (P, PAGE, D_LATENT))
+    if latent_std != 1.0:
+        latent *= np.float32(latent_std)
+    rope = _normal_f32(rng, (P, PAGE, D_ROPE))
+    if rope_std != 1.0:
+        rope *= np.float32(rope_std)
+    q_bits = f32_to_bf16_bits(q)
+    del q
+
+    kv_scale = None
+    if kv_dtype == "bf16":
+        cache = np.empty((P, PAGE, D_QK), dtype=np.uint16)
+        cache[..., :D_LATENT] = f32_to_bf16_bits(latent)
+        cache[..., D_LATENT:] = f32_to_bf16_bits(rope)
+    elif kv_dtype == "fp8_e4m3fn":
+        cache = np.empty((P, PAGE, D_QK), dtype=np.uint8)
+        kv_scale = np.empty((P, PAGE), dtype=np.float32)
+        step = 1024
+        for p0 in range(0, P, step):
+            p1 = min(P, p0 + step)
+            x = np.concatenate([latent[p0:p1], rope[p0:p1]], axis=-1)
+            amax = np.abs(x).max(axis=-1)
+            s = np.where(amax > 0, amax / np.float32(E4M3FN_MAX), np.float32(1.0)).astype(np.float32)
+            kv_scale[p0:p1] = s
+            cache[p0:p1] = f32_to_e4m3fn(x / s[..., None])
+    else:
+        raise ValueError(kv_dtype)
+    del latent, rope
+
+    if poison:
+        nan = BF16_NAN if kv_dtype == "bf16" else E4M3FN_NAN
+        referenced = np.zeros(P, dtype=bool)
+        for b in range(batch):
+            referenced[block_table[b, :npages[b]]] = True
+            tail = int(seqlens[b]) % PAGE
+            if tail:
+                last = block_table[b, npages[b] - 1]
+                cache[last, tail:] = nan
+                if kv_scale is not None:
+                    kv_scale[last, tail:] = np.nan
+        cache[~referenced] = nan
+        if kv_scale is not None:
+            kv_scale[~referenced] = np.nan
+    return Workload(name=name, q=q_bits, cache=cache, kv_scale=kv_scale, block_table=block_table, seqlens=seqlens,
+                    s_q=s_q, num_heads=num_heads, causal=causal)
+
+
+def ragged_seqlens(rng: np.random.Generator, batch: int, lo: int = 128, hi: int = 32768) -> np.ndarray:
+    """Per-request lengths drawn log-uniform in [lo, hi]."""
+    x = np.exp(rng.uniform(math.log(lo), math.log(hi), batch))
+    return np.clip(np.rint(x), lo, hi).astype(np.int32)
+
+
+# The five measured/parity configurations (descriptions are the workload names used everywhere).
+CONFIGS = {
+    "tiny_b1_h16_l256": dict(batch=1, num_heads=16, seqlen=256, seed=1, permute_pages=False),
+    "dsv3_b64_h128_l4096": dict(batch=64, num_heads=128, seqlen=4096, seed=2, latent_std=0.5),
+    "ragged_b128_h128_l128_32768": dict(batch=128, num_heads=128, seqlen="ragged", seed=3),
+    "mtp_b32_h128_sq2_l8192": dict(batch=32, num_heads=128, seqlen=8192, seed=4, s_q=2, causal=True),
+    "fp8_b128_h128_l16384": dict(batch=128, num_heads=128, seqlen=16384, seed=5, kv_dtype="fp8_e4m3fn"),
+}
+HEADLINE = "dsv3_b64_h128_l4096"
+
+
+def make_config(name: str, **overrides) -> Workload:
+    cfg = dict(CONFIGS[name])
+    cfg.update(overrides)
+    seed = cfg.pop("seed")
+    rng = np.random.default_rng(seed)
+    seqlen = cfg.pop("seqlen")
+    batch = cfg["batch"]
+    if seqlen == "ragged":
+        seqlens = ragged_seqlens(rng, batch)
+    else:
+        seqlens = np.full(batch, seqlen, dtype=np.int32)
+    return make_workload(name, seqlens=seqlens, rng=rng, **cfg)
