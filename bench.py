@@ -1,0 +1,209 @@
+#!/usr/bin/env python3
+"""Benchmark of one MLA absorb-path decode step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--copies C] [--no-cpu]
+
+A step is the whole hot path over one batch of synthetic inputs already
+resident in HBM: the split plan, the attention kernel over the paged cache and
+the LSE combine.  The timed region holds exactly K steps between device
+synchronisations.  The cache is cycled over C independent copies so repeats
+cannot be served from the 256 MB last-level cache (C is chosen so the copies
+total at least twice that, unless given).
+
+Prints one JSON line.  ``value`` is algorithmic TFLOP/s of the whole step;
+``roofline`` describes the attention kernel alone (its launches are timed with
+HIP events on the stream it runs on); ``cpu_baseline`` is the fp64 oracle run
+on a bounded sample of the same workload's rows on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+HBM_PEAK_GBPS = 8000.0            # MI355X HBM3E
+BF16_MFMA_PEAK_TFLOPS = 2500.0    # MI355X dense bf16
+MALL_BYTES = 256 << 20            # last-level (Infinity) cache
+D_LATENT, D_ROPE, D_NOPE, D_V = 512, 64, 128, 128
+
+
+# ---------------------------------------------------------------- algorithmic accounting
+def pair_flops_absorb(H, dc=D_LATENT, dr=D_ROPE):
+    """FLOPs per (query token, cached token) pair on the absorb path: a (dc+dr)-wide score and a
+    dc-wide weighted sum for each of H heads (handbook FLOP script)."""
+    return 2 * H * (dc + dr) + 2 * H * dc
+
+
+def pair_flops_expand(H, dn=D_NOPE, dr=D_ROPE, dv=D_V):
+    return 2 * H * (dn + dr) + 2 * H * dv
+
+
+def expand_flops_per_cached_token(H, dc=D_LATENT, dn=D_NOPE, dv=D_V):
+    return 2 * dc * H * (dn + dv)
+
+
+def absorb_flops_per_new_token(H, dc=D_LATENT, dn=D_NOPE, dv=D_V):
+    return 2 * H * dn * dc + 2 * H * dc * dv
+
+
+def causal_pairs(q, k):
+    """(query, key) pairs when q new tokens follow and are counted in k tokens, causal among the new ones."""
+    return q * k - q * (q - 1) // 2
+
+
+def kv_bytes_per_token(dtype="bf16", dc=D_LATENT, dr=D_ROPE):
+    """Cache bytes read per cached token: 2 bytes per number in bf16; 1 per number plus a 4-byte scale in FP8."""
+    return (dc + dr) * 2 if dtype == "bf16" else (dc + dr) + 4
+
+
+def workload_counts(seqlens, H, s_q, causal, kv_dtype="bf16"):
+    """(FLOPs, KV bytes, total algorithmic bytes) of one decode step over these requests."""
+    pairs = 0
+    for L in seqlens:
+        pairs += causal_pairs(s_q, int(L)) if causal else s_q * int(L)
+    flops = pairs * pair_flops_absorb(H)
+    kv = sum(int(L) for L in seqlens) * kv_bytes_per_token(kv_dtype)
+    B = len(seqlens)
+    io = B * s_q * H * (D_LATENT + D_ROPE) * 2 + B * s_q * H * D_LATENT * 2 + B * s_q * H * 4
+    tables = B * 4 + sum(-(-int(L) // 64) for L in seqlens) * 4
+    return flops, kv, kv + io + tables
+
+
+# ---------------------------------------------------------------- benchmark
+def _parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default=None)
+    ap.add_argument("--copies", type=int, default=0, help="independent cache copies to cycle (0 = auto)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target duration of the CPU baseline sample")
+    return ap.parse_args()
+
+
+def cpu_baseline(wl, target_s):
+    """fp64 oracle on a bounded sample of rows; returns the dict for the JSON line."""
+    import numpy as np
+    from oracle import oracle as O
+    total = wl.batch * wl.s_q * wl.num_heads
+    rng = np.random.default_rng(0)
+
+    def run(n):
+        rows = np.sort(rng.choice(total, size=min(n, total), replace=False)).astype(np.int64)
+        t0 = time.perf_counter()
+        O.attend(wl.q, wl.cache, wl.block_table, wl.seqlens, softmax_scale=wl.softmax_scale, causal=wl.causal,
+                 kv_scale=wl.kv_scale, rows=rows)
+        dt = time.perf_counter() - t0
+        H, s_q = wl.num_heads, wl.s_q
+        flops = 0
+        for r in rows:
+            b, i = int(r) // (s_q * H), (int(r) // H) % s_q
+            L = int(wl.seqlens[b])
+            n = (L - s_q + 1 + i) if wl.causal else L
+            flops += n * pair_flops_absorb(1)
+        return len(rows), dt, flops
+
+    n0, dt0, _ = run(max(8, O.num_threads()))
+    n = int(min(total, max(n0, n0 * target_s / max(dt0, 1e-3))))
+    n, dt, flops = run(n)
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": O.num_threads(), "kind": "oracle",
+            "sample": f"{n} of {total} query rows (fp64, {dt:.1f} s)"}
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1"}))
+        return 2
+    import numpy as np
+    import torch
+    import workloads as W
+    import mla_latent_kv_fwd_amd as M
+
+    name = args.config or W.HEADLINE
+    wl = W.make_config(name)
+    dev = torch.device("cuda")
+    kv_np = wl.cache.view(np.int16) if wl.cache.dtype == np.uint16 else wl.cache
+    kv_bytes_total = wl.cache.nbytes + (0 if wl.kv_scale is None else wl.kv_scale.nbytes)
+    copies = args.copies or max(1, math.ceil(2 * MALL_BYTES / kv_bytes_total))
+    kvs = [torch.from_numpy(kv_np).to(dev) for _ in range(copies)]
+    kss = [None if wl.kv_scale is None else torch.from_numpy(wl.kv_scale).to(dev) for _ in range(copies)]
+    q = torch.from_numpy(wl.q.view(np.int16)).to(dev)
+    bt = torch.from_numpy(wl.block_table).to(dev)
+    sl = torch.from_numpy(wl.seqlens).to(dev)
+    dec = M.MlaDecode(batch=wl.batch, seqlen_q=wl.s_q, num_heads=wl.num_heads, num_pages=wl.num_pages,
+                      max_blocks_per_seq=wl.block_table.shape[1], causal=wl.causal,
+                      kv_dtype=M.MLA_KV_FP8_E4M3FN if wl.kv_dtype == "fp8_e4m3fn" else M.MLA_KV_BF16,
+                      softmax_scale=float(wl.softmax_scale))
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        dec.plan(sl)
+        if ev is not None:
+            ev[1].record(stream)
+        dec.decode(q, kvs[i % copies], bt, sl, kss[i % copies])
+        if ev is not None:
+            ev[2].record(stream)
+        dec.combine()
+        if ev is not None:
+            ev[3].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # Timed region: exactly `steps` steps, synchronised on both sides.
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    plan_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    dec_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    comb_ms = [e[2].elapsed_time(e[3]) for e in evs]
+    ms_per_step = wall * 1e3 / args.steps
+    flops, kv_bytes, alg_bytes = workload_counts(wl.seqlens, wl.num_heads, wl.s_q, wl.causal, wl.kv_dtype)
+    dec_avg = float(np.mean(dec_ms))
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    kv_gbps = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    dec_gbps = alg_bytes / (dec_avg * 1e-3) / 1e9
+    dec_tflops = flops / (dec_avg * 1e-3) / 1e12
+    mfma_bound = flops / (BF16_MFMA_PEAK_TFLOPS * 1e12) > alg_bytes / (HBM_PEAK_GBPS * 1e9)
+    if mfma_bound:
+        roof = {"bound": "mfma", "achieved": round(dec_tflops, 2), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(dec_tflops / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None}
+    else:
+        roof = {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": None}
+    flags = dec.flags()
+    line = {
+        "metric": "MLA decode TFLOP/s + effective KV GB/s (% roofline), B=64 H=128 L=4096 bf16",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": name, "batch": wl.batch, "heads": wl.num_heads, "seqlen_q": wl.s_q,
+                   "seqlens_sum": int(wl.seqlens.sum()), "kv_dtype": wl.kv_dtype, "page": 64, "cache_copies": copies},
+        "kv_gbps": round(kv_gbps, 1), "kv_frac_hbm": round(kv_gbps / HBM_PEAK_GBPS, 4),
+        "tflops_frac_mfma": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+        "kernel_ms": {"plan": round(float(np.mean(plan_ms)), 5), "decode": round(dec_avg, 5),
+                      "combine": round(float(np.mean(comb_ms)), 5)},
+        "roofline": roof,
+        "flags": flags,
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

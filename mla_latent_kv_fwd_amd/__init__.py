@@ -1,0 +1,168 @@
+"""Python binding of libmla_decode.so: MLA absorb-path decode on MI355X (gfx950).
+
+Argument marshalling only.  Every step of the decode runs in the HIP kernels of
+the shared library; this module never computes attention itself, and it raises
+if the library is missing.  PyTorch supplies device memory and streams.
+
+The entry points carry the names of the C ABI (include/mla_decode.h):
+``mla_get_workspace``, ``mla_decode_fwd``, ``mla_splitkv_combine``,
+``mla_workspace_flags``.  ``MlaDecode`` wraps them for torch tensors.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmla_decode.so")
+
+MLA_OK = 0
+MLA_ERR_INVALID_ARG = -1
+MLA_ERR_UNSUPPORTED = -2
+MLA_ERR_WORKSPACE_TOO_SMALL = -3
+MLA_ERR_HIP = -4
+MLA_KV_BF16 = 0
+MLA_KV_FP8_E4M3FN = 1
+MLA_FLAG_SEQLEN_CLAMPED = 0x1
+MLA_FLAG_BAD_BLOCK = 0x2
+
+HEAD_DIM_QK = 576
+HEAD_DIM_V = 512
+PAGE_SIZE = 64
+SOFTMAX_SCALE = 1.0 / math.sqrt(128 + 64)
+
+EXPORTED_SYMBOLS = ("mla_get_workspace", "mla_decode_fwd", "mla_splitkv_combine", "mla_workspace_flags",
+                    "mla_status_string")
+
+
+class MlaError(RuntimeError):
+    def __init__(self, fn: str, status: int, message: str):
+        super().__init__(f"{fn}: {message} ({status})")
+        self.status = status
+
+
+class DecodeParams(ctypes.Structure):
+    """Mirror of mla_decode_params."""
+    _fields_ = [("batch", ctypes.c_int32), ("seqlen_q", ctypes.c_int32), ("num_heads", ctypes.c_int32),
+                ("head_dim_qk", ctypes.c_int32), ("head_dim_v", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("num_pages", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
+                ("causal", ctypes.c_int32), ("softmax_scale", ctypes.c_float), ("num_workgroups", ctypes.c_int32)]
+
+
+def make_params(*, batch, seqlen_q, num_heads, num_pages, max_blocks_per_seq, kv_dtype=MLA_KV_BF16, causal=False,
+                softmax_scale=SOFTMAX_SCALE, num_workgroups=0, head_dim_qk=HEAD_DIM_QK, head_dim_v=HEAD_DIM_V,
+                page_size=PAGE_SIZE) -> DecodeParams:
+    return DecodeParams(batch, seqlen_q, num_heads, head_dim_qk, head_dim_v, page_size, num_pages,
+                        max_blocks_per_seq, kv_dtype, int(bool(causal)), softmax_scale, num_workgroups)
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m mla_latent_kv_fwd_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    pp = ctypes.POINTER(DecodeParams)
+    lib.mla_get_workspace.argtypes = [pp, vp, vp, ctypes.POINTER(sz), vp]
+    lib.mla_decode_fwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
+    lib.mla_splitkv_combine.argtypes = [pp, vp, sz, vp, vp, vp]
+    lib.mla_workspace_flags.argtypes = [vp, ctypes.POINTER(ctypes.c_uint32), vp]
+    lib.mla_status_string.argtypes = [ctypes.c_int]
+    lib.mla_status_string.restype = ctypes.c_char_p
+    for name in ("mla_get_workspace", "mla_decode_fwd", "mla_splitkv_combine", "mla_workspace_flags"):
+        getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != MLA_OK:
+        raise MlaError(fn, status, load_library().mla_status_string(status).decode())
+
+
+def mla_get_workspace(params: DecodeParams, seqlens_ptr: int = 0, workspace_ptr: int = 0,
+                      workspace_bytes: int = 0, stream: int = 0) -> int:
+    """Size query (workspace_ptr == 0) or plan launch; returns the required size in bytes."""
+    nbytes = ctypes.c_size_t(workspace_bytes)
+    _check("mla_get_workspace", load_library().mla_get_workspace(
+        ctypes.byref(params), seqlens_ptr or None, workspace_ptr or None, ctypes.byref(nbytes), stream or None))
+    return nbytes.value
+
+
+def mla_decode_fwd(params: DecodeParams, q_ptr: int, kv_ptr: int, kv_scale_ptr: int, block_table_ptr: int,
+                   seqlens_ptr: int, workspace_ptr: int, workspace_bytes: int, out_ptr: int, lse_ptr: int,
+                   stream: int = 0) -> None:
+    _check("mla_decode_fwd", load_library().mla_decode_fwd(
+        ctypes.byref(params), q_ptr or None, kv_ptr or None, kv_scale_ptr or None, block_table_ptr or None,
+        seqlens_ptr or None, workspace_ptr or None, workspace_bytes, out_ptr or None, lse_ptr or None,
+        stream or None))
+
+
+def mla_splitkv_combine(params: DecodeParams, workspace_ptr: int, workspace_bytes: int, out_ptr: int,
+                        lse_ptr: int, stream: int = 0) -> None:
+    _check("mla_splitkv_combine", load_library().mla_splitkv_combine(
+        ctypes.byref(params), workspace_ptr or None, workspace_bytes, out_ptr or None, lse_ptr or None,
+        stream or None))
+
+
+def mla_workspace_flags(workspace_ptr: int, stream: int = 0) -> int:
+    flags = ctypes.c_uint32(0)
+    _check("mla_workspace_flags", load_library().mla_workspace_flags(workspace_ptr or None, ctypes.byref(flags),
+                                                                     stream or None))
+    return flags.value
+
+
+class MlaDecode:
+    """One decode configuration bound to torch tensors on the current HIP device.
+
+    ``plan(seqlens)`` runs the split plan; ``__call__`` runs decode + combine and
+    returns (out bf16 [B, s_q, H, 512], lse fp32 [B, s_q, H]).  Buffers are
+    allocated once, here, by torch; the library allocates nothing.
+    """
+
+    def __init__(self, *, batch, seqlen_q, num_heads, num_pages, max_blocks_per_seq, kv_dtype=MLA_KV_BF16,
+                 causal=False, softmax_scale=SOFTMAX_SCALE, num_workgroups=0, device="cuda"):
+        import torch
+        self.torch = torch
+        self.params = make_params(batch=batch, seqlen_q=seqlen_q, num_heads=num_heads, num_pages=num_pages,
+                                  max_blocks_per_seq=max_blocks_per_seq, kv_dtype=kv_dtype, causal=causal,
+                                  softmax_scale=softmax_scale, num_workgroups=num_workgroups)
+        self.device = torch.device(device)
+        self.workspace_bytes = mla_get_workspace(self.params)
+        # 256-byte aligned: the caching allocator hands out 512-byte aligned blocks.
+        self.workspace = torch.empty(self.workspace_bytes, dtype=torch.uint8, device=self.device)
+        self.out = torch.empty((batch, seqlen_q, num_heads, HEAD_DIM_V), dtype=torch.bfloat16, device=self.device)
+        self.lse = torch.empty((batch, seqlen_q, num_heads), dtype=torch.float32, device=self.device)
+
+    def _stream(self) -> int:
+        return self.torch.cuda.current_stream(self.device).cuda_stream
+
+    def plan(self, seqlens) -> None:
+        mla_get_workspace(self.params, seqlens.data_ptr(), self.workspace.data_ptr(), self.workspace_bytes,
+                          self._stream())
+
+    def decode(self, q, kv_cache, block_table, seqlens, kv_scale=None) -> None:
+        mla_decode_fwd(self.params, q.data_ptr(), kv_cache.data_ptr(), 0 if kv_scale is None else kv_scale.data_ptr(),
+                       block_table.data_ptr(), seqlens.data_ptr(), self.workspace.data_ptr(), self.workspace_bytes,
+                       self.out.data_ptr(), self.lse.data_ptr(), self._stream())
+
+    def combine(self) -> None:
+        mla_splitkv_combine(self.params, self.workspace.data_ptr(), self.workspace_bytes, self.out.data_ptr(),
+                            self.lse.data_ptr(), self._stream())
+
+    def __call__(self, q, kv_cache, block_table, seqlens, kv_scale=None, plan=True):
+        if plan:
+            self.plan(seqlens)
+        self.decode(q, kv_cache, block_table, seqlens, kv_scale)
+        self.combine()
+        return self.out, self.lse
+
+    def flags(self) -> int:
+        return mla_workspace_flags(self.workspace.data_ptr(), self._stream())

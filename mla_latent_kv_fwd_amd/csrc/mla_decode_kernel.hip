@@ -1,0 +1,338 @@
+// mla_decode_kernel.hip -- MLA absorb-path decode over a paged latent cache on
+// gfx950 (MI355X).
+//
+// What it computes, per query row r of request b and the cached tokens t the row
+// may see: s_t = scale * q~_r . [c_t ; k^R_t] (one 576-wide dot product: latent
+// part plus RoPE part), softmax over t, out_r = sum_t p_t c_t (the 512-wide
+// latent is the value), lse_r = ln sum_t exp(s_t).  ("MLA inference: two
+// computation paths and FlashMLA", section "Two equivalent paths": score
+// equation and path two; FlashMLA guide, Architecture step 3: the two score
+// parts summed and scaled by 1/sqrt(192); step 4: online softmax.)
+//
+// How it maps onto CDNA4.  A persistent workgroup of 8 waves owns up to 128
+// query rows (heads x new tokens) of one request and walks its stretch of
+// pages (the split plan).  All 128 rows share each cached token, so one token
+// read from HBM feeds 128 rows: the handbook's "Decode attention becomes a
+// compute problem" section -- heads as the M dimension, the latent as K, one
+// block handling all heads and a stretch of KV.
+//   * Pages stream HBM -> LDS with direct-to-LDS loads (no VGPR staging) into a
+//     ring of 4 slots of 32 tokens (4 x 36 KiB), three slots in flight.
+//   * Each wave holds its 16 rows of q~ in registers (18 MFMA B-fragments) and
+//     computes S^T = KV . q~^T with v_mfma_f32_16x16x32_bf16: tokens are M and
+//     rows are N, so every lane owns one row and the softmax statistics need two
+//     cross-lane swaps (the four 16-lane groups share a row).
+//   * O^T = V^T . P^T on the same MFMA: V^T fragments come straight from the
+//     token-major LDS slot through the gfx950 transposing LDS read, P^T is the
+//     score accumulator converted to bf16 in place, and O^T keeps lane = row,
+//     so the softmax rescale is a per-lane scalar.  Two waves share each SIMD,
+//     so one wave's softmax overlaps the other's MFMAs, and each wave fits in
+//     256 registers (q~ 72, O 128, scores 8, the rest working set).
+//   * The running maximum is rescaled lazily: O and the normaliser are only
+//     rescaled when a new maximum exceeds the reference by more than 2^8.
+//   * Tokens past the request's length are never loaded (their rows are
+//     replaced by the last valid token) and are masked to -inf, so stale or NaN
+//     bytes in a partly used last page cannot reach the output.
+#include <hip/hip_runtime.h>
+
+#define MLA_HD __host__ __device__
+#include "mla_launch.h"
+#include "mla_workspace.h"
+
+namespace mla {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr int kChunk = 32;                         // tokens per LDS slot
+constexpr int kSlots = 4;                          // ring depth
+constexpr int kRowBytes = kHeadDimQK * 2;          // 1152 bytes per bf16 token row
+constexpr int kGranPerRow = kRowBytes / 16;        // 72 16-byte granules
+constexpr int kSlotBytes = kChunk * kRowBytes;     // 36864
+constexpr int kSlotBlocks = kSlotBytes / 1024;     // 36 blocks of 64 granules (one wave-wide load each)
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRowsPerWave = kRowsPerBlock / kWaves;  // 16
+constexpr int kKSteps = kHeadDimQK / 32;           // 18 MFMA K-steps for QK
+constexpr int kDimTiles = kHeadDimV / 16;          // 32 16-wide output tiles
+constexpr float kLazyRescale = 8.0f;               // log2 of the largest p kept unrescaled
+constexpr float kLn2 = 0.69314718055994531f;
+
+static_assert(kSlots * kSlotBytes <= 160 * 1024, "LDS ring must fit in 160 KiB");
+static_assert(kRowsPerWave == 16, "one 16x16x32 MFMA column block per wave");
+
+// s_waitcnt immediate for "vector memory counter <= n", other counters untouched.
+#define VMCNT(n) ((((n) & 15) | (((n) >> 4) << 14)) | (7 << 4) | (15 << 8))
+
+// XOR swizzle of the low 3 bits of a row's 16-byte granule index.  With 64
+// four-byte LDS banks, a 16-lane QK read (16 consecutive tokens, one granule)
+// and a 32-lane transposing PV read (8 consecutive tokens, two granules) both
+// land on 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int swz(int tok) { return (tok & 6) | ((tok >> 3) & 1); }
+
+// One direct-to-LDS 16-byte load per lane: lane i writes LDS[m0 + 16 i].
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "memory");
+}
+
+// Direct-to-LDS loads this wave issues per slot: 36 blocks over 8 waves.
+__device__ __forceinline__ int dma_per_slot(int wave) { return wave < kSlotBlocks - 4 * kWaves ? 5 : 4; }
+
+// Fill one LDS slot with 32 consecutive token rows starting at src (all in one
+// page).  Rows at or past `valid` repeat row valid-1 (never read stale bytes).
+__device__ __forceinline__ void load_chunk(const char* src, int valid, uint32_t slot_lds, int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < 5; i++) {
+    const int blk = i * kWaves + wave;    // 1 KiB block of the slot this instruction fills
+    if (blk < kSlotBlocks) {
+      const int gi = blk * 64 + lane;     // granule index within the slot
+      const int tok = gi / kGranPerRow;
+      const int phys = gi - tok * kGranPerRow;
+      const int logical = phys ^ swz(tok);
+      const int src_tok = tok < valid ? tok : valid - 1;
+      dma16(src + src_tok * kRowBytes + logical * 16, slot_lds + blk * 1024);
+    }
+  }
+}
+
+// Max / sum over the four 16-lane groups that share a row.
+__device__ __forceinline__ float row_max(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float row_sum(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ bf16x8_t lds_read_b128(const char LDS_AS* p) {
+  return *reinterpret_cast<const bf16x8_t LDS_AS*>(p);
+}
+__device__ __forceinline__ i16x4_t lds_read_tr16(const char LDS_AS* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<i16x4_t LDS_AS*>(const_cast<char LDS_AS*>(p)));
+}
+
+__global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem_raw[kSlots * kSlotBytes];
+  char LDS_AS* smem = (char LDS_AS*)(smem_raw);
+  const uint32_t smem_addr = (uint32_t)(uintptr_t)smem;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15;   // row of this lane within the wave (and token row of the QK A-operand)
+  const int q = lane >> 4;   // 16-lane group
+
+  // blockIdx -> (stretch, row block).  Consecutive stretches (pieces of the same
+  // request) are kept on one XCD: blocks are dealt to the 8 XCDs round robin,
+  // so block i runs on XCD i % 8.
+  const int nblk = gridDim.x;
+  int lin = blockIdx.x;
+  if ((nblk & 7) == 0) lin = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
+  const int stretch = lin / a.nrb;
+  const int rb = lin - stretch * a.nrb;
+
+  Header* hdr = reinterpret_cast<Header*>(a.ws + a.lay.header);
+  const WgInfo wg = reinterpret_cast<const WgInfo*>(a.ws + a.lay.wg_info)[stretch];
+  const ReqInfo* reqs = reinterpret_cast<const ReqInfo*>(a.ws + a.lay.req_info);
+  if (wg.page_begin >= wg.page_end) return;
+
+  const int row_local = wave * kRowsPerWave + n;
+  const int row = rb * kRowsPerBlock + row_local;
+  const bool row_ok = row < a.rows;
+  const int qi = row_ok ? row / a.num_heads : 0;   // which new token this row belongs to
+  const int ndma = dma_per_slot(wave);
+
+  // Per-lane LDS byte offsets within a slot.
+  // QK A-operand: token 16tt + n, logical granule 4k + q -> physical 8(k>>1) + ((4(k&1)) ^ y).
+  const int y = q ^ swz(n);
+  const int qk_off0 = n * kRowBytes + ((0 ^ y) << 4);
+  const int qk_off1 = n * kRowBytes + ((4 ^ y) << 4);
+  // PV A-operand (V^T) through the transposing read: this lane supplies token
+  // 4q + (lane>>2 & 3) (+16 for the second read) and dims 16d + 4(lane & 3),
+  // i.e. logical granule 2d + (lane>>1 & 1) -> physical 8(d>>2) + ((2(d&3)) ^ z).
+  int pv_off[4];
+  {
+    const int tr = 4 * q + ((lane >> 2) & 3);
+    const int z = ((lane >> 1) & 1) ^ swz(tr);
+#pragma unroll
+    for (int dm = 0; dm < 4; dm++) pv_off[dm] = tr * kRowBytes + (((2 * dm) ^ z) << 4) + (lane & 1) * 8;
+  }
+
+  int gpage = wg.page_begin;
+  int b = wg.b_begin;
+  bool first_segment = true;
+  while (gpage < wg.page_end && b < a.batch) {
+    const ReqInfo rq = reqs[b];
+    if (rq.npages == 0) { b++; continue; }
+    const int pg0 = gpage - rq.page_first;
+    const int req_end = rq.page_first + rq.npages;
+    const int pg1 = (wg.page_end < req_end ? wg.page_end : req_end) - rq.page_first;
+    const int split = first_segment ? wg.ne_prefix - rq.ne_lo : 0;
+    const int L = rq.seqlen;
+    const int t_lo = pg0 * kPageSize;
+    const int t_hi = pg1 * kPageSize < L ? pg1 * kPageSize : L;
+    const int nchunks = (t_hi - t_lo + kChunk - 1) / kChunk;
+    const int n_vis = a.causal ? L - a.seqlen_q + 1 + qi : L;      // keys this lane's row may see
+    const int min_vis = a.causal ? L - a.seqlen_q + 1 : L;          // smallest over the request's rows
+    const int32_t* bt = a.block_table + (size_t)b * a.max_blocks;
+    const char* kv = reinterpret_cast<const char*>(a.kv);
+
+    // Queries: 18 B-fragments, q~[row][32k + 8q .. +8).
+    bf16x8_t qf[kKSteps];
+    {
+      const bf16x8_t* qrow =
+          reinterpret_cast<const bf16x8_t*>(a.q + ((size_t)b * a.rows + (row_ok ? row : 0)) * kHeadDimQK) + q;
+#pragma unroll
+      for (int k = 0; k < kKSteps; k++) {
+        bf16x8_t v = qrow[4 * k];
+        if (!row_ok) v = bf16x8_t{};
+        qf[k] = v;
+      }
+    }
+    // Everyone is done with the previous segment's slots; the query loads have landed.
+    __builtin_amdgcn_s_waitcnt(VMCNT(0));
+    __syncthreads();
+
+    auto issue = [&](int c) {
+      const int t0 = t_lo + c * kChunk;
+      int page = bt[t0 / kPageSize];
+      if (page < 0 || page >= a.num_pages) {
+        if (tid == 0) atomicOr(&hdr->flags, 2u);
+        page = 0;
+      }
+      const char* src = kv + ((size_t)page * kPageSize + (t0 % kPageSize)) * kRowBytes;
+      const int valid = t_hi - t0 < kChunk ? t_hi - t0 : kChunk;
+      load_chunk(src, valid, smem_addr + (c % kSlots) * kSlotBytes, wave, lane);
+    };
+    for (int c = 0; c < kSlots - 1 && c < nchunks; c++) issue(c);
+
+    float m_ref = -INFINITY;   // reference maximum (log2 units), same in all lanes of a row
+    float lsum = 0.f;          // this lane's part of the normaliser
+    f32x4_t o[kDimTiles];
+#pragma unroll
+    for (int d = 0; d < kDimTiles; d++) o[d] = f32x4_t{};
+
+    for (int c = 0; c < nchunks; c++) {
+      // Wait until this wave's loads of chunk c have landed (later chunks may stay in flight).
+      const int ahead = (nchunks - 1 < c + kSlots - 2 ? nchunks - 1 : c + kSlots - 2) - c;
+      if (ndma == 5) {
+        if (ahead >= 2) __builtin_amdgcn_s_waitcnt(VMCNT(10));
+        else if (ahead == 1) __builtin_amdgcn_s_waitcnt(VMCNT(5));
+        else __builtin_amdgcn_s_waitcnt(VMCNT(0));
+      } else {
+        if (ahead >= 2) __builtin_amdgcn_s_waitcnt(VMCNT(8));
+        else if (ahead == 1) __builtin_amdgcn_s_waitcnt(VMCNT(4));
+        else __builtin_amdgcn_s_waitcnt(VMCNT(0));
+      }
+      __syncthreads();   // every wave's part of chunk c is in LDS; slot (c-1)%4 is free
+      if (c + kSlots - 1 < nchunks) issue(c + kSlots - 1);
+
+      const char LDS_AS* slot = smem + (c % kSlots) * kSlotBytes;
+      const int t0 = t_lo + c * kChunk;
+
+      // S^T[token][row] over the 576 dims, two 16-token tiles.
+      f32x4_t s0 = f32x4_t{}, s1 = f32x4_t{};
+#pragma unroll
+      for (int k = 0; k < kKSteps; k++) {
+        const int off = ((k & 1) ? qk_off1 : qk_off0) + (k >> 1) * 128;
+        const bf16x8_t a0 = lds_read_b128(slot + off);
+        const bf16x8_t a1 = lds_read_b128(slot + 16 * kRowBytes + off);
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[k], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[k], s1, 0, 0, 0);
+      }
+
+      // Scale, mask, online softmax.  s0[i] is token 4q + i, s1[i] token 16 + 4q + i.
+      float v[8];
+      float cmax = -INFINITY;
+      const bool need_mask = t0 + kChunk > min_vis;
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        float x = (i < 4 ? s0[i] : s1[i - 4]) * a.scale_log2;
+        if (need_mask && t0 + 16 * (i >> 2) + 4 * q + (i & 3) >= n_vis) x = -INFINITY;
+        v[i] = x;
+        cmax = fmaxf(cmax, x);
+      }
+      cmax = row_max(cmax);
+      const bool need = cmax > m_ref + kLazyRescale;
+      if (__builtin_amdgcn_ballot_w64(need)) {
+        const float m_new = need ? cmax : m_ref;
+        const float alpha = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+        lsum *= alpha;
+#pragma unroll
+        for (int d = 0; d < kDimTiles; d++) o[d] *= alpha;
+        m_ref = m_new;
+      }
+      const float mu = m_ref == -INFINITY ? 0.f : m_ref;
+      bf16x8_t pb;
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        const float p = __builtin_amdgcn_exp2f(v[i] - mu);
+        lsum += p;
+        pb[i] = (__bf16)p;
+      }
+
+      // O^T[dim][row] += V^T[dim][token] . P^T[token][row], 32 tiles of 16 dims.
+#pragma unroll
+      for (int d = 0; d < kDimTiles; d++) {
+        const int off = pv_off[d & 3] + (d >> 2) * 128;
+        const i16x4_t lo = lds_read_tr16(slot + off);
+        const i16x4_t hi = lds_read_tr16(slot + 16 * kRowBytes + off);
+        const i16x8_t av = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av), pb, o[d], 0, 0, 0);
+      }
+    }
+
+    // Finalise this segment: normalise, then write the output rows or a partial.
+    {
+      const float ltot = row_sum(lsum);
+      const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+      const float lse_v = ltot > 0.f ? (m_ref + __builtin_amdgcn_logf(ltot)) * kLn2 : -INFINITY;
+      if (rq.nsplit <= 1) {
+        if (row_ok) {
+          uint16_t* orow = a.out + ((size_t)b * a.rows + row) * kHeadDimV + 4 * q;
+#pragma unroll
+          for (int d = 0; d < kDimTiles; d++) {
+            bf16x4_t w;
+#pragma unroll
+            for (int r = 0; r < 4; r++) w[r] = (__bf16)(o[d][r] * inv);
+            *reinterpret_cast<bf16x4_t*>(orow + 16 * d) = w;
+          }
+          if (q == 0) a.lse[(size_t)b * a.rows + row] = lse_v;
+        }
+      } else {
+        const int slot_id = rq.slot_off + split;
+        if (slot_id < 2 * a.nwg) {
+          const size_t pidx = ((size_t)slot_id * a.nrb + rb) * kRowsPerBlock + row_local;
+          float* prow = reinterpret_cast<float*>(a.ws + a.lay.part_out) + pidx * kHeadDimV + 4 * q;
+#pragma unroll
+          for (int d = 0; d < kDimTiles; d++) *reinterpret_cast<f32x4_t*>(prow + 16 * d) = o[d] * inv;
+          if (q == 0) reinterpret_cast<float*>(a.ws + a.lay.part_lse)[pidx] = lse_v;
+        }
+      }
+    }
+    gpage = rq.page_first + pg1;
+    b++;
+    first_segment = false;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& a, bool fp8, hipStream_t stream) {
+  if (fp8) return hipErrorNotSupported;
+  void* args[] = {(void*)&a};
+  return hipLaunchKernel((const void*)mla_decode_bf16_kernel, dim3(a.nwg * a.nrb), dim3(kThreads), args, 0, stream);
+}
+
+}  // namespace mla

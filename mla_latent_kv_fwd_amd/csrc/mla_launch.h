@@ -1,0 +1,31 @@
+// mla_launch.h -- host-side launchers of the library's kernels.  Internal.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mla_workspace.h"
+
+namespace mla {
+
+// Everything the decode kernel reads, passed by value.
+struct DecodeArgs {
+  const uint16_t* q;          // bf16 [B][s_q][H][576]
+  const void* kv;             // [P][64][576] bf16 or E4M3FN
+  const float* kv_scale;      // [P][64] (FP8 only)
+  const int32_t* block_table; // [B][max_blocks]
+  char* ws;
+  Layout lay;
+  uint16_t* out;              // bf16 [B][s_q][H][512]
+  float* lse;                 // [B][s_q][H]
+  int batch, seqlen_q, num_heads, rows, nrb, nwg, num_pages, max_blocks, causal;
+  float scale_log2;           // softmax_scale * log2(e)
+};
+
+hipError_t launch_plan(const int32_t* seqlens, void* ws, const Layout& lay, int batch, int seqlen_q, int rows,
+                       int nwg, int max_blocks, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, bool fp8, hipStream_t stream);
+hipError_t launch_combine(const char* ws, const Layout& lay, int batch, int rows, uint16_t* out, float* lse,
+                          hipStream_t stream);
+
+}  // namespace mla
