@@ -69,11 +69,11 @@ static_assert(kRowsPerWave == 16, "one 16x16x32 MFMA column block per wave");
 // s_waitcnt immediate for "vector memory counter <= n", other counters untouched.
 #define VMCNT(n) ((((n) & 15) | (((n) >> 4) << 14)) | (7 << 4) | (15 << 8))
 
-// XOR swizzle of the low 3 bits of a row's 16-byte granule index.  With 64
-// four-byte LDS banks, a 16-lane QK read (16 consecutive tokens, one granule)
-// and a 32-lane transposing PV read (8 consecutive tokens, two granules) both
-// land on 16 distinct 16-byte bank groups.
-__device__ __forceinline__ int swz(int tok) { return (tok & 6) | ((tok >> 3) & 1); }
+// XOR swizzle of the low 3 bits of a row's 16-byte granule index by bits 1-2
+// of the token index.  Picked by timing every linear 4->3 bit swizzle on both
+// read patterns (a 16-token b128 QK read, an 8-token transposing PV read): this
+// one runs both at the LDS's linear-access rate.
+__device__ __forceinline__ int swz(int tok) { return tok & 6; }
 
 // One direct-to-LDS 16-byte load per lane: lane i writes LDS[m0 + 16 i].
 __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {
@@ -241,15 +241,23 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
       const char LDS_AS* slot = smem + (c % kSlots) * kSlotBytes;
       const int t0 = t_lo + c * kChunk;
 
-      // S^T[token][row] over the 576 dims, two 16-token tiles.
+      // S^T[token][row] over the 576 dims, two 16-token tiles.  Fragments are read
+      // one K-step ahead so each MFMA's operands are already in flight.
       f32x4_t s0 = f32x4_t{}, s1 = f32x4_t{};
+      bf16x8_t a0 = lds_read_b128(slot + qk_off0);
+      bf16x8_t a1 = lds_read_b128(slot + 16 * kRowBytes + qk_off0);
 #pragma unroll
       for (int k = 0; k < kKSteps; k++) {
-        const int off = ((k & 1) ? qk_off1 : qk_off0) + (k >> 1) * 128;
-        const bf16x8_t a0 = lds_read_b128(slot + off);
-        const bf16x8_t a1 = lds_read_b128(slot + 16 * kRowBytes + off);
+        bf16x8_t n0 = a0, n1 = a1;
+        if (k + 1 < kKSteps) {
+          const int off = (((k + 1) & 1) ? qk_off1 : qk_off0) + ((k + 1) >> 1) * 128;
+          n0 = lds_read_b128(slot + off);
+          n1 = lds_read_b128(slot + 16 * kRowBytes + off);
+        }
         s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[k], s0, 0, 0, 0);
         s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[k], s1, 0, 0, 0);
+        a0 = n0;
+        a1 = n1;
       }
 
       // Scale, mask, online softmax.  s0[i] is token 4q + i, s1[i] token 16 + 4q + i.
@@ -282,14 +290,22 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
         pb[i] = (__bf16)p;
       }
 
-      // O^T[dim][row] += V^T[dim][token] . P^T[token][row], 32 tiles of 16 dims.
-#pragma unroll
-      for (int d = 0; d < kDimTiles; d++) {
+      // O^T[dim][row] += V^T[dim][token] . P^T[token][row], 32 tiles of 16 dims,
+      // V^T fragments read two tiles ahead.
+      auto read_v = [&](int d) {
         const int off = pv_off[d & 3] + (d >> 2) * 128;
         const i16x4_t lo = lds_read_tr16(slot + off);
         const i16x4_t hi = lds_read_tr16(slot + 16 * kRowBytes + off);
-        const i16x8_t av = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av), pb, o[d], 0, 0, 0);
+        return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+      bf16x8_t v0 = read_v(0), v1 = read_v(1);
+#pragma unroll
+      for (int d = 0; d < kDimTiles; d++) {
+        bf16x8_t v2 = v1;
+        if (d + 2 < kDimTiles) v2 = read_v(d + 2);
+        o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v0, pb, o[d], 0, 0, 0);
+        v0 = v1;
+        v1 = v2;
       }
     }
 
