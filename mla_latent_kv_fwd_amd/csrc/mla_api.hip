@@ -15,7 +15,6 @@ namespace {
 
 using namespace mla;
 
-constexpr int kMaxWorkgroups = 1 << 16;
 constexpr int kMaxDevices = 64;
 
 // Compute-unit count per device, queried once.
@@ -63,7 +62,7 @@ int resolve_nwg(const mla_decode_params* p, int* nwg) {
   const int64_t max_pages = (int64_t)p->batch * p->max_blocks_per_seq;
   int64_t v = want;
   if (v > max_pages) v = max_pages;
-  if (v > kMaxWorkgroups / nrb) v = kMaxWorkgroups / nrb;
+  if (v > kMaxStretches) v = kMaxStretches;
   *nwg = (int)(v < 1 ? 1 : v);
   return MLA_OK;
 }

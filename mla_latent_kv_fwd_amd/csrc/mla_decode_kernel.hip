@@ -76,8 +76,13 @@ static_assert(kRowsPerWave == 16, "one 16x16x32 MFMA column block per wave");
 __device__ __forceinline__ int swz(int tok) { return tok & 6; }
 
 // One direct-to-LDS 16-byte load per lane: lane i writes LDS[m0 + 16 i].
+// The compiler's hazard recognizer does not see inside inline asm, so the asm
+// supplies the wait states itself: an LDS-DMA load reading M0 right after M0 is
+// written needs 1, and a vector memory instruction reading an SGPR that a VALU
+// instruction (readfirstlane) just wrote needs 5.
 __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {
-  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr))
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr),
+               "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr))
                : "memory");
 }
 

@@ -17,7 +17,8 @@ constexpr int kPageSize = 64;       // tokens per page
 constexpr int kRowsPerBlock = 128;  // query rows one workgroup holds (4 waves x 32)
 constexpr int kMaxHeads = 128;
 constexpr int kMaxSeqlenQ = 8;
-constexpr int kMaxBatch = 1 << 20;
+constexpr int kMaxBatch = 8192;      // requests per step (the plan keeps its arrays in LDS)
+constexpr int kMaxStretches = 4096;  // persistent workgroups per row block
 constexpr int kPlanCostPerRequest = 2;  // fixed cost of a request segment, in pages
 constexpr uint32_t kMagic = 0x4D4C4131u;  // "MLA1"
 
@@ -55,7 +56,7 @@ struct Header {
 
 // Byte offsets of every region; all 256-byte aligned.
 struct Layout {
-  size_t header, wg_info, req_info, cum_cost, bounds, part_lse, part_out, total;
+  size_t header, wg_info, req_info, part_lse, part_out, total;
 };
 
 MLA_HD inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -70,8 +71,6 @@ MLA_HD inline Layout make_layout(int batch, int rows, int nwg) {
   l.header = off;   off = align256(off + sizeof(Header));
   l.wg_info = off;  off = align256(off + sizeof(WgInfo) * size_t(nwg));
   l.req_info = off; off = align256(off + sizeof(ReqInfo) * size_t(batch));
-  l.cum_cost = off; off = align256(off + sizeof(int64_t) * size_t(batch + 1));
-  l.bounds = off;   off = align256(off + sizeof(int32_t) * 2 * size_t(nwg + 1));
   l.part_lse = off; off = align256(off + sizeof(float) * slots * nrb * kRowsPerBlock);
   l.part_out = off; off = align256(off + sizeof(float) * slots * nrb * kRowsPerBlock * kHeadDimV);
   l.total = off;
