@@ -48,6 +48,22 @@ typedef short i16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 #define LDS_AS __attribute__((address_space(3)))
+// Read-only for the whole kernel: reads through this address space become scalar
+// loads, counted by lgkmcnt rather than vmcnt, so they never wait on the
+// direct-to-LDS loads in flight.
+#define CONST_AS __attribute__((address_space(4)))
+
+// Load a plain struct of 32-bit fields through the constant address space.
+template <typename T>
+__device__ __forceinline__ T load_const(const void* p) {
+  static_assert(sizeof(T) % 4 == 0, "32-bit fields only");
+  T r;
+  const int CONST_AS* s = (const int CONST_AS*)p;
+  int* d = reinterpret_cast<int*>(&r);
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(T) / 4); i++) d[i] = s[i];
+  return r;
+}
 
 constexpr int kChunk = 32;                         // tokens per LDS slot
 constexpr int kSlots = 4;                          // ring depth
@@ -75,35 +91,37 @@ static_assert(kRowsPerWave == 16, "one 16x16x32 MFMA column block per wave");
 // one runs both at the LDS's linear-access rate.
 __device__ __forceinline__ int swz(int tok) { return tok & 6; }
 
-// One direct-to-LDS 16-byte load per lane: lane i writes LDS[m0 + 16 i].
-// The compiler's hazard recognizer does not see inside inline asm, so the asm
-// supplies the wait states itself: an LDS-DMA load reading M0 right after M0 is
-// written needs 1, and a vector memory instruction reading an SGPR that a VALU
-// instruction (readfirstlane) just wrote needs 5.
-__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {
-  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr),
+// One direct-to-LDS 16-byte load per lane from base + voff (base: wave-uniform,
+// in SGPRs): lane i writes LDS[m0 + 16 i].  The hazard recognizer does not see
+// inside inline asm, so the asm supplies the wait states itself: an LDS-DMA load
+// reading M0 right after M0 is written needs 1, and a vector memory instruction
+// reading an SGPR that a VALU instruction just wrote needs 5.
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds_addr) {
+  // readfirstlane returns int: go through uint32_t so the low half is zero-extended.
+  const uint64_t b = (uint64_t)base;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+  const uint64_t sbase = ((uint64_t)hi << 32) | (uint64_t)lo;
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
                "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr))
                : "memory");
 }
 
-// Direct-to-LDS loads this wave issues per slot: 36 blocks over 8 waves.
+// Direct-to-LDS loads this wave issues per slot: 36 one-KiB blocks over 8 waves.
 __device__ __forceinline__ int dma_per_slot(int wave) { return wave < kSlotBlocks - 4 * kWaves ? 5 : 4; }
 
-// Fill one LDS slot with 32 consecutive token rows starting at src (all in one
-// page).  Rows at or past `valid` repeat row valid-1 (never read stale bytes).
-__device__ __forceinline__ void load_chunk(const char* src, int valid, uint32_t slot_lds, int wave, int lane) {
-#pragma unroll
-  for (int i = 0; i < 5; i++) {
-    const int blk = i * kWaves + wave;    // 1 KiB block of the slot this instruction fills
-    if (blk < kSlotBlocks) {
-      const int gi = blk * 64 + lane;     // granule index within the slot
-      const int tok = gi / kGranPerRow;
-      const int phys = gi - tok * kGranPerRow;
-      const int logical = phys ^ swz(tok);
-      const int src_tok = tok < valid ? tok : valid - 1;
-      dma16(src + src_tok * kRowBytes + logical * 16, slot_lds + blk * 1024);
-    }
-  }
+// Fill part i of one LDS slot with 32 consecutive token rows starting at src
+// (all in one page).  LDS granule blk*64 + lane is row tok, physical granule
+// phys, which holds logical granule phys ^ swz(tok).  Rows at or past `valid`
+// repeat row valid-1, so bytes past a request's end are never read.
+__device__ __forceinline__ void load_chunk_part(const char* src, int valid, uint32_t slot_lds, int i, int wave,
+                                                int lane) {
+  const int blk = i * kWaves + wave;    // 1 KiB block of the slot this instruction fills
+  const int gi = blk * 64 + lane;       // granule index within the slot
+  const int tok = gi / kGranPerRow;
+  const int phys = gi - tok * kGranPerRow;
+  const int src_tok = tok < valid ? tok : valid - 1;
+  dma16(src, (uint32_t)(src_tok * kRowBytes + ((phys ^ swz(tok)) << 4)), slot_lds + blk * 1024);
 }
 
 // Max / sum over the four 16-lane groups that share a row.
@@ -148,8 +166,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
   const int rb = lin - stretch * a.nrb;
 
   Header* hdr = reinterpret_cast<Header*>(a.ws + a.lay.header);
-  const WgInfo wg = reinterpret_cast<const WgInfo*>(a.ws + a.lay.wg_info)[stretch];
-  const ReqInfo* reqs = reinterpret_cast<const ReqInfo*>(a.ws + a.lay.req_info);
+  const WgInfo wg = load_const<WgInfo>(a.ws + a.lay.wg_info + sizeof(WgInfo) * stretch);
+  const char* reqs = a.ws + a.lay.req_info;
   if (wg.page_begin >= wg.page_end) return;
 
   const int row_local = wave * kRowsPerWave + n;
@@ -178,7 +196,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
   int b = wg.b_begin;
   bool first_segment = true;
   while (gpage < wg.page_end && b < a.batch) {
-    const ReqInfo rq = reqs[b];
+    const ReqInfo rq = load_const<ReqInfo>(reqs + sizeof(ReqInfo) * b);
     if (rq.npages == 0) { b++; continue; }
     const int pg0 = gpage - rq.page_first;
     const int req_end = rq.page_first + rq.npages;
@@ -190,7 +208,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
     const int nchunks = (t_hi - t_lo + kChunk - 1) / kChunk;
     const int n_vis = a.causal ? L - a.seqlen_q + 1 + qi : L;      // keys this lane's row may see
     const int min_vis = a.causal ? L - a.seqlen_q + 1 : L;          // smallest over the request's rows
-    const int32_t* bt = a.block_table + (size_t)b * a.max_blocks;
+    const int32_t CONST_AS* bt = (const int32_t CONST_AS*)(a.block_table + (size_t)b * a.max_blocks);
     const char* kv = reinterpret_cast<const char*>(a.kv);
 
     // Queries: 18 B-fragments, q~[row][32k + 8q .. +8).
@@ -218,7 +236,10 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
       }
       const char* src = kv + ((size_t)page * kPageSize + (t0 % kPageSize)) * kRowBytes;
       const int valid = t_hi - t0 < kChunk ? t_hi - t0 : kChunk;
-      load_chunk(src, valid, smem_addr + (c % kSlots) * kSlotBytes, wave, lane);
+      const uint32_t slot_lds = smem_addr + (c % kSlots) * kSlotBytes;
+#pragma unroll
+      for (int i = 0; i < 5; i++)
+        if (i < ndma) load_chunk_part(src, valid, slot_lds, i, wave, lane);
     };
     for (int c = 0; c < kSlots - 1 && c < nchunks; c++) issue(c);
 
