@@ -116,10 +116,14 @@ int mla_get_workspace(const mla_decode_params* p, const int32_t* seqlens, void* 
  * q:           bf16 [batch][seqlen_q][num_heads][576], the absorbed queries
  * kv_cache:    [num_pages][64][576] of bf16 (MLA_KV_BF16) or E4M3FN bytes (MLA_KV_FP8_E4M3FN);
  *              token t of request b is row t % 64 of page block_table[b][t / 64]
- * kv_scale:    fp32 [num_pages][64], per-token scale of an FP8 cache; must be NULL for bf16
+ * kv_scale:    fp32 [num_pages][64], per-token scale of an FP8 cache, 16-byte aligned; must be NULL for bf16.
+ *              The kernel widens each code to bf16 exactly and applies the scale in fp32 to the
+ *              token's score and to its softmax weight before that weight is rounded to bf16.
  * block_table: int32 [batch][max_blocks_per_seq]; entries past the last page of a request are not read
  * seqlens:     int32 [batch], the same buffer contents the plan read
  * out:         bf16 [batch][seqlen_q][num_heads][512]
+ * Alignment: q, kv_cache and kv_scale 16 bytes, out 8 bytes, workspace 256 bytes
+ * (MLA_ERR_INVALID_ARG otherwise).
  * lse:         fp32 [batch][seqlen_q][num_heads], natural log of the softmax normaliser of the scaled scores
  * Rows of requests the plan did not split are final after this call; the others
  * are final after mla_splitkv_combine.

@@ -40,7 +40,6 @@ int validate(const mla_decode_params* p) {
   if (p->head_dim_qk != kHeadDimQK || p->head_dim_v != kHeadDimV || p->page_size != kPageSize)
     return MLA_ERR_UNSUPPORTED;
   if (p->seqlen_q > kMaxSeqlenQ || p->num_heads > kMaxHeads) return MLA_ERR_UNSUPPORTED;
-  if (p->kv_dtype == MLA_KV_FP8_E4M3FN) return MLA_ERR_UNSUPPORTED;
   // page positions and token counts are int32 inside the kernels
   if ((int64_t)p->batch * p->max_blocks_per_seq >= ((int64_t)1 << 31) / kPageSize) return MLA_ERR_UNSUPPORTED;
   if ((int64_t)p->num_pages >= ((int64_t)1 << 31) / kPageSize) return MLA_ERR_UNSUPPORTED;
@@ -110,7 +109,8 @@ int mla_decode_fwd(const mla_decode_params* p, const void* q, const void* kv_cac
   if (st != MLA_OK) return st;
   if (!q || !kv_cache || !block_table || !seqlens || !workspace || !out || !lse) return MLA_ERR_INVALID_ARG;
   if ((p->kv_dtype == MLA_KV_FP8_E4M3FN) != (kv_scale != nullptr)) return MLA_ERR_INVALID_ARG;
-  if (((uintptr_t)q & 15) || ((uintptr_t)kv_cache & 15) || ((uintptr_t)out & 7) || ((uintptr_t)workspace & 255))
+  if (((uintptr_t)q & 15) || ((uintptr_t)kv_cache & 15) || ((uintptr_t)out & 7) || ((uintptr_t)workspace & 255) ||
+      ((uintptr_t)kv_scale & 15))
     return MLA_ERR_INVALID_ARG;
   int nwg = 0;
   if ((st = resolve_nwg(p, &nwg)) != MLA_OK) return st;

@@ -369,12 +369,319 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
   }
 }
 
+// ---------------------------------------------------------------------------
+// FP8 (E4M3FN) cache with one fp32 scale per token: kv_t = decode(code_t) * scale_t.
+// The codes are widened to bf16 exactly (every E4M3FN value is a bf16 value)
+// and fed to the same bf16 MFMAs; the scale is applied where it is exact in
+// fp32 -- to column t of the scores, and to p_t before P is rounded to bf16 for
+// the P . V product.  The normaliser sums the unscaled p_t.
+// ---------------------------------------------------------------------------
+constexpr int kRowBytes8 = kHeadDimQK;                  // 576 one-byte codes per token
+constexpr int kChunk8 = 32;                             // tokens per slot
+constexpr int kSlots8 = 8;                              // ring depth (a slot is half a bf16 slot)
+constexpr int kSlotBytes8 = kChunk8 * kRowBytes8;       // 18432
+constexpr int kSlotBlocks8 = kSlotBytes8 / 1024;        // 18 one-KiB loads
+constexpr int kGranPerRow8 = kRowBytes8 / 16;           // 36
+constexpr int kScaleBytes8 = kChunk8 * 4;               // 128 bytes of scales per slot
+constexpr int kLdsBytes8 = kSlots8 * (kSlotBytes8 + kScaleBytes8);
+constexpr int kSuperSteps8 = kHeadDimQK / 64;           // 9 reads of 16 codes per token tile
+static_assert(kLdsBytes8 <= 160 * 1024, "FP8 ring must fit in 160 KiB");
+static_assert(kSlotBlocks8 + 1 <= 3 * kWaves, "slot loads (codes + one scale block) fit three per wave");
+
+// XOR swizzle of the low 2 bits of a 576-byte row's 16-byte granule index.
+// Found by a search over linear functions of the token bits under a 64-bank
+// model: it makes both the score read (16 tokens x 16 bytes) and the
+// transposing value read (8 tokens x 16 bytes per 16 lanes) conflict free.
+__device__ __forceinline__ int swz8(int tok) { return ((tok >> 2) & 1) | ((((tok >> 3) ^ (tok >> 4)) & 1) << 1); }
+
+// Loads per wave per slot: 18 code blocks and one scale block over 8 waves.
+__device__ __forceinline__ int dma_per_slot8(int wave) { return wave < 3 ? 3 : 2; }
+
+// Part i of a slot fill: block i*8 + wave.  Blocks 0..17 carry 32 token rows of
+// codes (granule g of the slot is token g / 36, physical granule g % 36 holding
+// logical granule (g % 36) ^ swz8(token)); block 18 carries the 32 scales (8
+// lanes x 4).  Rows at or past `valid` repeat row valid-1.
+__device__ __forceinline__ void load_chunk_part8(const char* src, const float* scale_src, int valid,
+                                                 uint32_t slot_lds, uint32_t scale_lds, int i, int wave, int lane) {
+  const int blk = i * kWaves + wave;
+  if (blk < kSlotBlocks8) {
+    const int gi = blk * 64 + lane;
+    const int tok = gi / kGranPerRow8;
+    const int phys = gi - tok * kGranPerRow8;
+    const int src_tok = tok < valid ? tok : valid - 1;
+    dma16(src, (uint32_t)(src_tok * kRowBytes8 + ((phys ^ swz8(tok)) << 4)), slot_lds + blk * 1024);
+  } else if (blk == kSlotBlocks8 && lane < kChunk8 / 4) {
+    dma16(scale_src, (uint32_t)(lane * 16), scale_lds);
+  }
+}
+
+// Four E4M3FN codes (one dword) -> four bf16, exactly.
+__device__ __forceinline__ void fp8x4_to_bf16(uint32_t w, bf16x8_t& out, int at) {
+  const auto lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+  const auto hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+  out[at + 0] = lo[0];
+  out[at + 1] = lo[1];
+  out[at + 2] = hi[0];
+  out[at + 3] = hi[1];
+}
+
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(kThreads, 1) void mla_decode_fp8_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem_raw[kLdsBytes8];
+  char LDS_AS* smem = (char LDS_AS*)(smem_raw);
+  const uint32_t smem_addr = (uint32_t)(uintptr_t)smem;
+  const uint32_t scale_addr = smem_addr + kSlots8 * kSlotBytes8;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15;
+  const int q = lane >> 4;
+
+  const int nblk = gridDim.x;
+  int lin = blockIdx.x;
+  if ((nblk & 7) == 0) lin = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
+  const int stretch = lin / a.nrb;
+  const int rb = lin - stretch * a.nrb;
+
+  Header* hdr = reinterpret_cast<Header*>(a.ws + a.lay.header);
+  const WgInfo wg = load_const<WgInfo>(a.ws + a.lay.wg_info + sizeof(WgInfo) * stretch);
+  const char* reqs = a.ws + a.lay.req_info;
+  if (wg.page_begin >= wg.page_end) return;
+
+  const int row_local = wave * kRowsPerWave + n;
+  const int row = rb * kRowsPerBlock + row_local;
+  const bool row_ok = row < a.rows;
+  const int qi = row_ok ? row / a.num_heads : 0;
+  const int ndma = dma_per_slot8(wave);
+
+  // Score read: token 16tt + n, logical granule 4j + q (16 codes: dims
+  // 64j + 16q .. +15) -> physical 4j + (q ^ swz8(token)).
+  const int qk8_off0 = n * kRowBytes8 + ((q ^ swz8(n)) << 4);
+  const int qk8_off1 = (16 + n) * kRowBytes8 + ((q ^ swz8(16 + n)) << 4);
+  // Value read (transposing, 8 tokens x 16 codes per 16 lanes): this lane
+  // supplies row r = (lane & 15) >> 1, i.e. token 4q + (r & 3) + 16 (r >> 2),
+  // and bytes 8 (lane & 1) of granule d (dims 16d .. 16d+15), physical
+  // granule (d & ~3) | ((d & 3) ^ swz8(token)).
+  int pv8_off[4];
+  {
+    const int r = (lane & 15) >> 1;
+    const int tok = 4 * q + (r & 3) + 16 * (r >> 2);
+#pragma unroll
+    for (int dm = 0; dm < 4; dm++) pv8_off[dm] = tok * kRowBytes8 + ((dm ^ swz8(tok)) << 4) + (lane & 1) * 8;
+  }
+
+  int gpage = wg.page_begin;
+  int b = wg.b_begin;
+  bool first_segment = true;
+  while (gpage < wg.page_end && b < a.batch) {
+    const ReqInfo rq = load_const<ReqInfo>(reqs + sizeof(ReqInfo) * b);
+    if (rq.npages == 0) { b++; continue; }
+    const int pg0 = gpage - rq.page_first;
+    const int req_end = rq.page_first + rq.npages;
+    const int pg1 = (wg.page_end < req_end ? wg.page_end : req_end) - rq.page_first;
+    const int split = first_segment ? wg.ne_prefix - rq.ne_lo : 0;
+    const int L = rq.seqlen;
+    const int t_lo = pg0 * kPageSize;
+    const int t_hi = pg1 * kPageSize < L ? pg1 * kPageSize : L;
+    const int nchunks = (t_hi - t_lo + kChunk8 - 1) / kChunk8;
+    const int n_vis = a.causal ? L - a.seqlen_q + 1 + qi : L;
+    const int min_vis = a.causal ? L - a.seqlen_q + 1 : L;
+    const int32_t CONST_AS* bt = (const int32_t CONST_AS*)(a.block_table + (size_t)b * a.max_blocks);
+    const char* kv = reinterpret_cast<const char*>(a.kv);
+
+    // Queries, permuted to match the 16-code reads: fragment 2j + h holds
+    // q~[row][64j + 16q + 8h .. +8), the dims that read j's half h widens to.
+    bf16x8_t qf[kKSteps];
+    {
+      const bf16x8_t* qrow =
+          reinterpret_cast<const bf16x8_t*>(a.q + ((size_t)b * a.rows + (row_ok ? row : 0)) * kHeadDimQK);
+#pragma unroll
+      for (int j = 0; j < kSuperSteps8; j++)
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+          bf16x8_t v = qrow[8 * j + 2 * q + h];
+          if (!row_ok) v = bf16x8_t{};
+          qf[2 * j + h] = v;
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(VMCNT(0));
+    __syncthreads();
+
+    auto issue = [&](int c) {
+      const int t0 = t_lo + c * kChunk8;
+      int page = bt[t0 / kPageSize];
+      const bool bad = page < 0 || page >= a.num_pages;
+      page = bad ? 0 : page;
+      if (bad && tid == 0) atomicOr(&hdr->flags, 2u);
+      const size_t tok0 = (size_t)page * kPageSize + (t0 % kPageSize);
+      const char* src = kv + tok0 * kRowBytes8;
+      const float* ssrc = a.kv_scale + tok0;
+      const int valid = t_hi - t0 < kChunk8 ? t_hi - t0 : kChunk8;
+      const int slot = c % kSlots8;
+#pragma unroll
+      for (int i = 0; i < 3; i++)
+        if (i < ndma)
+          load_chunk_part8(src, ssrc, valid, smem_addr + slot * kSlotBytes8, scale_addr + slot * kScaleBytes8, i,
+                           wave, lane);
+    };
+    for (int c = 0; c < kSlots8 - 1 && c < nchunks; c++) issue(c);
+
+    float m_ref = -INFINITY;
+    float lsum = 0.f;
+    f32x4_t o[kDimTiles];
+#pragma unroll
+    for (int d = 0; d < kDimTiles; d++) o[d] = f32x4_t{};
+
+    for (int c = 0; c < nchunks; c++) {
+      // Wait for this wave's loads of chunk c; up to six later chunks stay in flight.
+      const int ahead = (nchunks - 1 < c + kSlots8 - 2 ? nchunks - 1 : c + kSlots8 - 2) - c;
+      if (ndma == 3) {
+        switch (ahead) {
+          case 6: __builtin_amdgcn_s_waitcnt(VMCNT(18)); break;
+          case 5: __builtin_amdgcn_s_waitcnt(VMCNT(15)); break;
+          case 4: __builtin_amdgcn_s_waitcnt(VMCNT(12)); break;
+          case 3: __builtin_amdgcn_s_waitcnt(VMCNT(9)); break;
+          case 2: __builtin_amdgcn_s_waitcnt(VMCNT(6)); break;
+          case 1: __builtin_amdgcn_s_waitcnt(VMCNT(3)); break;
+          default: __builtin_amdgcn_s_waitcnt(VMCNT(0)); break;
+        }
+      } else {
+        switch (ahead) {
+          case 6: __builtin_amdgcn_s_waitcnt(VMCNT(12)); break;
+          case 5: __builtin_amdgcn_s_waitcnt(VMCNT(10)); break;
+          case 4: __builtin_amdgcn_s_waitcnt(VMCNT(8)); break;
+          case 3: __builtin_amdgcn_s_waitcnt(VMCNT(6)); break;
+          case 2: __builtin_amdgcn_s_waitcnt(VMCNT(4)); break;
+          case 1: __builtin_amdgcn_s_waitcnt(VMCNT(2)); break;
+          default: __builtin_amdgcn_s_waitcnt(VMCNT(0)); break;
+        }
+      }
+      __syncthreads();   // chunk c is in LDS everywhere; slot (c-1) % 8 is free
+      if (c + kSlots8 - 1 < nchunks) issue(c + kSlots8 - 1);
+
+      const int slot_i = c % kSlots8;
+      const char LDS_AS* slot = smem + slot_i * kSlotBytes8;
+      const float LDS_AS* sc_lds = (const float LDS_AS*)(smem + kSlots8 * kSlotBytes8 + slot_i * kScaleBytes8);
+      const int t0 = t_lo + c * kChunk8;
+
+      // S^T over the 576 dims: each 16-code read widens to two A-fragments.
+      f32x4_t s0 = f32x4_t{}, s1 = f32x4_t{};
+#pragma unroll
+      for (int j = 0; j < kSuperSteps8; j++) {
+        const i32x4_t w0 = *reinterpret_cast<const i32x4_t LDS_AS*>(slot + qk8_off0 + 64 * j);
+        const i32x4_t w1 = *reinterpret_cast<const i32x4_t LDS_AS*>(slot + qk8_off1 + 64 * j);
+        bf16x8_t a0l, a0h, a1l, a1h;
+        fp8x4_to_bf16((uint32_t)w0[0], a0l, 0);
+        fp8x4_to_bf16((uint32_t)w0[1], a0l, 4);
+        fp8x4_to_bf16((uint32_t)w0[2], a0h, 0);
+        fp8x4_to_bf16((uint32_t)w0[3], a0h, 4);
+        fp8x4_to_bf16((uint32_t)w1[0], a1l, 0);
+        fp8x4_to_bf16((uint32_t)w1[1], a1l, 4);
+        fp8x4_to_bf16((uint32_t)w1[2], a1h, 0);
+        fp8x4_to_bf16((uint32_t)w1[3], a1h, 4);
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0l, qf[2 * j], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1l, qf[2 * j], s1, 0, 0, 0);
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0h, qf[2 * j + 1], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1h, qf[2 * j + 1], s1, 0, 0, 0);
+      }
+
+      // Token scales of this lane's eight tokens: 4q + i and 16 + 4q + i.
+      const f32x4_t sc0 = *reinterpret_cast<const f32x4_t LDS_AS*>(sc_lds + 4 * q);
+      const f32x4_t sc1 = *reinterpret_cast<const f32x4_t LDS_AS*>(sc_lds + 16 + 4 * q);
+      float v[8];
+      float cmax = -INFINITY;
+      const bool need_mask = t0 + kChunk8 > min_vis;
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        const float sc = i < 4 ? sc0[i] : sc1[i - 4];
+        float x = (i < 4 ? s0[i] : s1[i - 4]) * sc * a.scale_log2;
+        if (need_mask && t0 + 16 * (i >> 2) + 4 * q + (i & 3) >= n_vis) x = -INFINITY;
+        v[i] = x;
+        cmax = fmaxf(cmax, x);
+      }
+      cmax = row_max(cmax);
+      const bool need = cmax > m_ref + kLazyRescale;
+      if (__builtin_amdgcn_ballot_w64(need)) {
+        const float m_new = need ? cmax : m_ref;
+        const float alpha = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+        lsum *= alpha;
+#pragma unroll
+        for (int d = 0; d < kDimTiles; d++) o[d] *= alpha;
+        m_ref = m_new;
+      }
+      const float mu = m_ref == -INFINITY ? 0.f : m_ref;
+      bf16x8_t pb;
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        const float p = __builtin_amdgcn_exp2f(v[i] - mu);
+        lsum += p;
+        // a masked token's scale may be anything (past the request's end): keep its p at 0
+        const float sc = i < 4 ? sc0[i] : sc1[i - 4];
+        pb[i] = (__bf16)(v[i] == -INFINITY ? 0.f : p * sc);
+      }
+
+      // O^T += V^T . P'^T: one transposing read of 8 tokens x 16 codes per tile.
+      auto read_v8 = [&](int d) {
+        const i32x2_t w = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            reinterpret_cast<i32x2_t LDS_AS*>(const_cast<char LDS_AS*>(slot) + pv8_off[d & 3] + (d >> 2) * 64));
+        bf16x8_t r;
+        fp8x4_to_bf16((uint32_t)w[0], r, 0);
+        fp8x4_to_bf16((uint32_t)w[1], r, 4);
+        return r;
+      };
+      bf16x8_t v0 = read_v8(0), v1 = read_v8(1);
+#pragma unroll
+      for (int d = 0; d < kDimTiles; d++) {
+        bf16x8_t v2 = v1;
+        if (d + 2 < kDimTiles) v2 = read_v8(d + 2);
+        o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v0, pb, o[d], 0, 0, 0);
+        v0 = v1;
+        v1 = v2;
+      }
+    }
+
+    {
+      const float ltot = row_sum(lsum);
+      const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+      const float lse_v = ltot > 0.f ? (m_ref + __builtin_amdgcn_logf(ltot)) * kLn2 : -INFINITY;
+      if (rq.nsplit <= 1) {
+        if (row_ok) {
+          uint16_t* orow = a.out + ((size_t)b * a.rows + row) * kHeadDimV + 4 * q;
+#pragma unroll
+          for (int d = 0; d < kDimTiles; d++) {
+            bf16x4_t w;
+#pragma unroll
+            for (int r = 0; r < 4; r++) w[r] = (__bf16)(o[d][r] * inv);
+            *reinterpret_cast<bf16x4_t*>(orow + 16 * d) = w;
+          }
+          if (q == 0) a.lse[(size_t)b * a.rows + row] = lse_v;
+        }
+      } else {
+        const int slot_id = rq.slot_off + split;
+        if (slot_id < 2 * a.nwg) {
+          const size_t pidx = ((size_t)slot_id * a.nrb + rb) * kRowsPerBlock + row_local;
+          float* prow = reinterpret_cast<float*>(a.ws + a.lay.part_out) + pidx * kHeadDimV + 4 * q;
+#pragma unroll
+          for (int d = 0; d < kDimTiles; d++) *reinterpret_cast<f32x4_t*>(prow + 16 * d) = o[d] * inv;
+          if (q == 0) reinterpret_cast<float*>(a.ws + a.lay.part_lse)[pidx] = lse_v;
+        }
+      }
+    }
+    gpage = rq.page_first + pg1;
+    b++;
+    first_segment = false;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs& a, bool fp8, hipStream_t stream) {
-  if (fp8) return hipErrorNotSupported;
   void* args[] = {(void*)&a};
-  return hipLaunchKernel((const void*)mla_decode_bf16_kernel, dim3(a.nwg * a.nrb), dim3(kThreads), args, 0, stream);
+  const void* kern = fp8 ? (const void*)mla_decode_fp8_kernel : (const void*)mla_decode_bf16_kernel;
+  return hipLaunchKernel(kern, dim3(a.nwg * a.nrb), dim3(kThreads), args, 0, stream);
 }
 
 }  // namespace mla
