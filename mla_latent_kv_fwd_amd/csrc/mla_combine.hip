@@ -10,8 +10,14 @@
 //
 // Memory-bound: one 512-wide fp32 row per piece in, one bf16 row out.  A
 // workgroup of 256 threads handles two rows; each thread owns four consecutive
-// output columns (16-byte loads, 8-byte stores).
+// output columns (16-byte loads, 8-byte stores).  The pieces are merged in one
+// online pass (running maximum, normaliser and weighted sum, rescaled when the
+// maximum grows), so the LSEs and partial rows of a group of pieces are all
+// loaded before any of them is used: one memory latency per group instead of
+// an LSE round trip followed by the row loads.
 #include <hip/hip_runtime.h>
+
+#include <stddef.h>
 
 #define MLA_HD __host__ __device__
 #include "mla_launch.h"
@@ -23,9 +29,12 @@ namespace {
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 
+#define CONST_AS __attribute__((address_space(4)))
+
 constexpr int kThreads = 256;
 constexpr int kRowsPerWg = 2;
 constexpr int kThreadsPerRow = kThreads / kRowsPerWg;   // 128 threads x 4 columns = 512
+constexpr int kGroup = 4;                               // pieces loaded together
 
 __global__ __launch_bounds__(kThreads) void mla_combine_kernel(const char* __restrict__ ws, Layout lay, int rows,
                                                                uint16_t* __restrict__ out, float* __restrict__ lse) {
@@ -33,47 +42,61 @@ __global__ __launch_bounds__(kThreads) void mla_combine_kernel(const char* __res
   const int row = blockIdx.y * kRowsPerWg + threadIdx.x / kThreadsPerRow;
   const int col = (threadIdx.x % kThreadsPerRow) * 4;
   if (row >= rows) return;
-  const ReqInfo rq = reinterpret_cast<const ReqInfo*>(ws + lay.req_info)[b];
+  // Request info is uniform over the workgroup: scalar loads.
+  const int32_t CONST_AS* rqp = (const int32_t CONST_AS*)(ws + lay.req_info + sizeof(ReqInfo) * b);
+  const int npages = rqp[offsetof(ReqInfo, npages) / 4], nsplit = rqp[offsetof(ReqInfo, nsplit) / 4],
+            slot_off = rqp[offsetof(ReqInfo, slot_off) / 4];
   const size_t orow = (size_t)b * rows + row;
   bf16x4_t* dst = reinterpret_cast<bf16x4_t*>(out + orow * kHeadDimV + col);
 
-  if (rq.npages == 0) {   // a request with no tokens: defined empty result
+  if (npages == 0) {   // a request with no tokens: defined empty result
     *dst = bf16x4_t{};
     if (col == 0) lse[orow] = -INFINITY;
     return;
   }
-  if (rq.nsplit <= 1) return;   // written by the decode kernel
+  if (nsplit <= 1) return;   // written by the decode kernel
 
-  const Header* hdr = reinterpret_cast<const Header*>(ws + lay.header);
-  const int nrb = hdr->nrb;
-  if (rq.slot_off < 0 || rq.slot_off + rq.nsplit > hdr->max_slots) return;   // never true for a valid plan
+  const int32_t CONST_AS* hdr = (const int32_t CONST_AS*)(ws + lay.header);
+  const int nrb = hdr[offsetof(Header, nrb) / 4], max_slots = hdr[offsetof(Header, max_slots) / 4];
+  if (slot_off < 0 || slot_off + nsplit > max_slots) return;   // never true for a valid plan
   const int rb = row / kRowsPerBlock, rr = row % kRowsPerBlock;
   const float* plse = reinterpret_cast<const float*>(ws + lay.part_lse);
   const float* pout = reinterpret_cast<const float*>(ws + lay.part_out);
-  auto pidx = [&](int j) { return ((size_t)(rq.slot_off + j) * nrb + rb) * kRowsPerBlock + rr; };
+  auto pidx = [&](int j) { return ((size_t)(slot_off + j) * nrb + rb) * kRowsPerBlock + rr; };
 
-  float m = -INFINITY;
-  for (int j = 0; j < rq.nsplit; j++) m = fmaxf(m, plse[pidx(j)]);
+  float m = -INFINITY, z = 0.f;
+  f32x4_t acc = f32x4_t{};
+  for (int j0 = 0; j0 < nsplit; j0 += kGroup) {
+    float lj[kGroup];
+    f32x4_t oj[kGroup];
+#pragma unroll
+    for (int g = 0; g < kGroup; g++) {
+      const bool ok = j0 + g < nsplit;
+      lj[g] = ok ? plse[pidx(j0 + g)] : -INFINITY;
+      oj[g] = ok ? *reinterpret_cast<const f32x4_t*>(pout + pidx(j0 + g) * kHeadDimV + col) : f32x4_t{};
+    }
+#pragma unroll
+    for (int g = 0; g < kGroup; g++) {
+      if (lj[g] == -INFINITY) continue;   // an empty piece carries no weight; its row is not used
+      const float m2 = fmaxf(m, lj[g]);
+      const float keep = __expf(m - m2);  // 0 while m is still -inf
+      const float w = __expf(lj[g] - m2);
+      z = z * keep + w;
+      acc = acc * keep + w * oj[g];
+      m = m2;
+    }
+  }
   if (m == -INFINITY) {
     *dst = bf16x4_t{};
     if (col == 0) lse[orow] = -INFINITY;
     return;
   }
-  float z = 0.f;
-  for (int j = 0; j < rq.nsplit; j++) z += __expf(plse[pidx(j)] - m);
-  const float total = m + __logf(z);
-  f32x4_t acc = f32x4_t{};
-  for (int j = 0; j < rq.nsplit; j++) {
-    const float lj = plse[pidx(j)];
-    if (lj == -INFINITY) continue;
-    const float w = __expf(lj - total);
-    acc += w * *reinterpret_cast<const f32x4_t*>(pout + pidx(j) * kHeadDimV + col);
-  }
+  const float inv = 1.f / z;
   bf16x4_t r;
 #pragma unroll
-  for (int i = 0; i < 4; i++) r[i] = (__bf16)acc[i];
+  for (int i = 0; i < 4; i++) r[i] = (__bf16)(acc[i] * inv);
   *dst = r;
-  if (col == 0) lse[orow] = total;
+  if (col == 0) lse[orow] = m + __logf(z);
 }
 
 }  // namespace
