@@ -82,7 +82,55 @@ def _parse():
     ap.add_argument("--copies", type=int, default=0, help="independent cache copies to cycle (0 = auto)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target duration of the CPU baseline sample")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 1 GiB -> 1 GiB elementwise copy (calibrates the HBM byte counters)")
     return ap.parse_args()
+
+
+COPY_PROBE_BYTES = 1 << 30
+
+
+def copy_probe():
+    """Five launches of a plain elementwise kernel that reads 1 GiB and writes 1 GiB (fp32 negation):
+    the reference for scaling rocprofv3's FETCH_SIZE / WRITE_SIZE readings to bytes."""
+    import torch
+    n = COPY_PROBE_BYTES // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": COPY_PROBE_BYTES, "copy_probe_bytes_written": COPY_PROBE_BYTES,
+                      "launches": 5}))
+    return 0
+
+
+def kernel_source_digest():
+    import hashlib
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "mla_latent_kv_fwd_amd", "csrc",
+                        "mla_decode_kernel.hip")
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(workload, kv_dtype):
+    """HBM bytes per attention-kernel launch from the committed counter summary of this workload, or None
+    when there is none or the kernel source changed since the counters were taken."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", f"traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("- ") and ": " in line:
+                k, v = line[2:].split(": ", 1)
+                fields[k.strip().strip("`")] = v.strip().strip("`")
+    if fields.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    try:
+        return int(fields["decode_hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(wl, target_s):
@@ -119,6 +167,8 @@ def main():
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1"}))
         return 2
+    if args.copy_probe:
+        return copy_probe()
     import numpy as np
     import torch
     import workloads as W
@@ -180,10 +230,10 @@ def main():
     mfma_bound = flops / (BF16_MFMA_PEAK_TFLOPS * 1e12) > alg_bytes / (HBM_PEAK_GBPS * 1e9)
     if mfma_bound:
         roof = {"bound": "mfma", "achieved": round(dec_tflops, 2), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(dec_tflops / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None}
+                "frac": round(dec_tflops / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": measured_traffic(name, wl.kv_dtype)}
     else:
         roof = {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": None}
+                "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(name, wl.kv_dtype)}
     flags = dec.flags()
     line = {
         "metric": "MLA decode TFLOP/s + effective KV GB/s (% roofline), B=64 H=128 L=4096 bf16",
