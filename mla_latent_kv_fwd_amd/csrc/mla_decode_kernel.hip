@@ -124,6 +124,16 @@ __device__ __forceinline__ void load_chunk_part(const char* src, int valid, uint
   dma16(src, (uint32_t)(src_tok * kRowBytes + ((phys ^ swz(tok)) << 4)), slot_lds + blk * 1024);
 }
 
+// The lane index, hidden from the optimiser.  Per-lane address terms derived
+// from it where they are used are recomputed there (a few VALU operations)
+// instead of being hoisted and kept live across the segment loop, where they
+// would push the wave past 256 registers.
+__device__ __forceinline__ int opaque_lane() {
+  int l = __lane_id();
+  asm volatile("" : "+v"(l));
+  return l;
+}
+
 // Max / sum over the four 16-lane groups that share a row.
 __device__ __forceinline__ float row_max(float x) {
   auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -211,20 +221,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
     const int32_t CONST_AS* bt = (const int32_t CONST_AS*)(a.block_table + (size_t)b * a.max_blocks);
     const char* kv = reinterpret_cast<const char*>(a.kv);
 
-    // Queries: 18 B-fragments, q~[row][32k + 8q .. +8).
-    bf16x8_t qf[kKSteps];
-    {
-      const bf16x8_t* qrow =
-          reinterpret_cast<const bf16x8_t*>(a.q + ((size_t)b * a.rows + (row_ok ? row : 0)) * kHeadDimQK) + q;
-#pragma unroll
-      for (int k = 0; k < kKSteps; k++) {
-        bf16x8_t v = qrow[4 * k];
-        if (!row_ok) v = bf16x8_t{};
-        qf[k] = v;
-      }
-    }
-    // Everyone is done with the previous segment's slots; the query loads have landed.
-    __builtin_amdgcn_s_waitcnt(VMCNT(0));
+    // The previous segment's readers of the slots are done.
     __syncthreads();
 
     auto issue = [&](int c) {
@@ -242,6 +239,22 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
         if (i < ndma) load_chunk_part(src, valid, slot_lds, i, wave, lane);
     };
     for (int c = 0; c < kSlots - 1 && c < nchunks; c++) issue(c);
+
+    // Queries, loaded after the first page loads so that both latencies overlap;
+    // one wait covers them all (the compiler tracks only the query loads).
+    // 18 B-fragments, q~[row][32k + 8q .. +8).
+    bf16x8_t qf[kKSteps];
+    {
+      const bf16x8_t* qrow =
+          reinterpret_cast<const bf16x8_t*>(a.q + ((size_t)b * a.rows + (row_ok ? row : 0)) * kHeadDimQK) + q;
+#pragma unroll
+      for (int k = 0; k < kKSteps; k++) {
+        bf16x8_t v = qrow[4 * k];
+        if (!row_ok) v = bf16x8_t{};
+        qf[k] = v;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(VMCNT(0));
 
     float m_ref = -INFINITY;   // reference maximum (log2 units), same in all lanes of a row
     float lsum = 0.f;          // this lane's part of the normaliser
@@ -336,13 +349,20 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
     }
 
     // Finalise this segment: normalise, then write the output rows or a partial.
+    // Addresses are rebuilt from the lane here rather than hoisted out of the
+    // segment loop (64-bit pointers kept live across it would be spilled, and
+    // every reload would wait for all outstanding stores).
     {
       const float ltot = row_sum(lsum);
       const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
       const float lse_v = ltot > 0.f ? (m_ref + __builtin_amdgcn_logf(ltot)) * kLn2 : -INFINITY;
+      const int ol = opaque_lane();
+      const int orow_local = wave * kRowsPerWave + (ol & 15);
+      const int orow_g = rb * kRowsPerBlock + orow_local;
+      const int oq = ol >> 4;
       if (rq.nsplit <= 1) {
-        if (row_ok) {
-          uint16_t* orow = a.out + ((size_t)b * a.rows + row) * kHeadDimV + 4 * q;
+        if (orow_g < a.rows) {
+          uint16_t* orow = a.out + ((size_t)b * a.rows + orow_g) * kHeadDimV + 4 * oq;
 #pragma unroll
           for (int d = 0; d < kDimTiles; d++) {
             bf16x4_t w;
@@ -350,16 +370,16 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
             for (int r = 0; r < 4; r++) w[r] = (__bf16)(o[d][r] * inv);
             *reinterpret_cast<bf16x4_t*>(orow + 16 * d) = w;
           }
-          if (q == 0) a.lse[(size_t)b * a.rows + row] = lse_v;
+          if (oq == 0) a.lse[(size_t)b * a.rows + orow_g] = lse_v;
         }
       } else {
         const int slot_id = rq.slot_off + split;
         if (slot_id < 2 * a.nwg) {
-          const size_t pidx = ((size_t)slot_id * a.nrb + rb) * kRowsPerBlock + row_local;
-          float* prow = reinterpret_cast<float*>(a.ws + a.lay.part_out) + pidx * kHeadDimV + 4 * q;
+          const size_t pidx = ((size_t)slot_id * a.nrb + rb) * kRowsPerBlock + orow_local;
+          float* prow = reinterpret_cast<float*>(a.ws + a.lay.part_out) + pidx * kHeadDimV + 4 * oq;
 #pragma unroll
           for (int d = 0; d < kDimTiles; d++) *reinterpret_cast<f32x4_t*>(prow + 16 * d) = o[d] * inv;
-          if (q == 0) reinterpret_cast<float*>(a.ws + a.lay.part_lse)[pidx] = lse_v;
+          if (oq == 0) reinterpret_cast<float*>(a.ws + a.lay.part_lse)[pidx] = lse_v;
         }
       }
     }
@@ -492,22 +512,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_fp8_kernel(DecodeArgs 
     const int32_t CONST_AS* bt = (const int32_t CONST_AS*)(a.block_table + (size_t)b * a.max_blocks);
     const char* kv = reinterpret_cast<const char*>(a.kv);
 
-    // Queries, permuted to match the 16-code reads: fragment 2j + h holds
-    // q~[row][64j + 16q + 8h .. +8), the dims that read j's half h widens to.
-    bf16x8_t qf[kKSteps];
-    {
-      const bf16x8_t* qrow =
-          reinterpret_cast<const bf16x8_t*>(a.q + ((size_t)b * a.rows + (row_ok ? row : 0)) * kHeadDimQK);
-#pragma unroll
-      for (int j = 0; j < kSuperSteps8; j++)
-#pragma unroll
-        for (int h = 0; h < 2; h++) {
-          bf16x8_t v = qrow[8 * j + 2 * q + h];
-          if (!row_ok) v = bf16x8_t{};
-          qf[2 * j + h] = v;
-        }
-    }
-    __builtin_amdgcn_s_waitcnt(VMCNT(0));
+    // The previous segment's readers of the slots are done.
     __syncthreads();
 
     auto issue = [&](int c) {
@@ -528,6 +533,25 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_fp8_kernel(DecodeArgs 
                            wave, lane);
     };
     for (int c = 0; c < kSlots8 - 1 && c < nchunks; c++) issue(c);
+
+    // Queries, loaded after the first page loads so that both latencies overlap;
+    // one wait covers them all (the compiler tracks only the query loads).
+    // Queries, permuted to match the 16-code reads: fragment 2j + h holds
+    // q~[row][64j + 16q + 8h .. +8), the dims that read j's half h widens to.
+    bf16x8_t qf[kKSteps];
+    {
+      const bf16x8_t* qrow =
+          reinterpret_cast<const bf16x8_t*>(a.q + ((size_t)b * a.rows + (row_ok ? row : 0)) * kHeadDimQK);
+#pragma unroll
+      for (int j = 0; j < kSuperSteps8; j++)
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+          bf16x8_t v = qrow[8 * j + 2 * q + h];
+          if (!row_ok) v = bf16x8_t{};
+          qf[2 * j + h] = v;
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(VMCNT(0));
 
     float m_ref = -INFINITY;
     float lsum = 0.f;
@@ -643,13 +667,18 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_fp8_kernel(DecodeArgs 
       }
     }
 
+    // Finalise: addresses rebuilt from the lane (see the bf16 kernel).
     {
       const float ltot = row_sum(lsum);
       const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
       const float lse_v = ltot > 0.f ? (m_ref + __builtin_amdgcn_logf(ltot)) * kLn2 : -INFINITY;
+      const int ol = opaque_lane();
+      const int orow_local = wave * kRowsPerWave + (ol & 15);
+      const int orow_g = rb * kRowsPerBlock + orow_local;
+      const int oq = ol >> 4;
       if (rq.nsplit <= 1) {
-        if (row_ok) {
-          uint16_t* orow = a.out + ((size_t)b * a.rows + row) * kHeadDimV + 4 * q;
+        if (orow_g < a.rows) {
+          uint16_t* orow = a.out + ((size_t)b * a.rows + orow_g) * kHeadDimV + 4 * oq;
 #pragma unroll
           for (int d = 0; d < kDimTiles; d++) {
             bf16x4_t w;
@@ -657,16 +686,16 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_fp8_kernel(DecodeArgs 
             for (int r = 0; r < 4; r++) w[r] = (__bf16)(o[d][r] * inv);
             *reinterpret_cast<bf16x4_t*>(orow + 16 * d) = w;
           }
-          if (q == 0) a.lse[(size_t)b * a.rows + row] = lse_v;
+          if (oq == 0) a.lse[(size_t)b * a.rows + orow_g] = lse_v;
         }
       } else {
         const int slot_id = rq.slot_off + split;
         if (slot_id < 2 * a.nwg) {
-          const size_t pidx = ((size_t)slot_id * a.nrb + rb) * kRowsPerBlock + row_local;
-          float* prow = reinterpret_cast<float*>(a.ws + a.lay.part_out) + pidx * kHeadDimV + 4 * q;
+          const size_t pidx = ((size_t)slot_id * a.nrb + rb) * kRowsPerBlock + orow_local;
+          float* prow = reinterpret_cast<float*>(a.ws + a.lay.part_out) + pidx * kHeadDimV + 4 * oq;
 #pragma unroll
           for (int d = 0; d < kDimTiles; d++) *reinterpret_cast<f32x4_t*>(prow + 16 * d) = o[d] * inv;
-          if (q == 0) reinterpret_cast<float*>(a.ws + a.lay.part_lse)[pidx] = lse_v;
+          if (oq == 0) reinterpret_cast<float*>(a.ws + a.lay.part_lse)[pidx] = lse_v;
         }
       }
     }
