@@ -126,6 +126,26 @@ def test_short_lengths(torch, M, L):
     check(out, lse, ref_o, ref_l, f"L={L}")
 
 
+JUMP_SEQLENS = [1600, 900, 1100, 2000, 1800]
+JUMP_SPANS = [[(1200, 3, 1)],                              # mid-request, inside a page
+              [(896, 3, 1)],                               # in the ragged last page
+              [(0, 3, 1)],                                 # first chunk: later keys sit far below the maximum
+              [(600, 1, 1), (1300, 1, 1), (1999, 1, 1)],   # one jump, then more keys at the same level
+              [(1000, 3, 1), (1700, 1, 2)]]                # two jumps: two rescales of the running sums
+
+
+@pytest.mark.parametrize("nwg", [0, 1, 7])
+def test_score_jump_forces_rescale(torch, M, nwg):
+    """Scores that rise by ~9.4 (log2 units) partway through a request make the
+    running maximum rescale the accumulated output and normaliser, while the
+    earlier keys still carry ~40% of the softmax mass."""
+    wl = W.make_score_jump_workload("jump", seqlens=JUMP_SEQLENS, jumps=JUMP_SPANS, seed=41)
+    _say(f"score jumps nwg={nwg}")
+    out, lse, _ = run_gpu(torch, M, wl, num_workgroups=nwg)
+    ref_o, ref_l = oracle(wl)
+    check(out, lse, ref_o, ref_l, f"jump nwg={nwg}")
+
+
 def test_one_token_copies_latent_bits(torch, M):
     """With one visible token p = 1 exactly, so the bf16 output must equal the cached latent bit for bit."""
     wl = W.make_workload("one", batch=4, num_heads=128, seqlens=[1, 1, 1, 1], seed=3)

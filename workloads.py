@@ -104,8 +104,13 @@ def make_workload(name: str, *, batch: int, num_heads: int, seqlens: Sequence[in
                   causal: bool = False, seed: int = 0, latent_std: float = 1.0, q_std: float = 1.0,
                   rope_std: float = 1.0, kv_dtype: str = "bf16", permute_pages: bool = True,
                   spare_pages: int = 0, max_blocks: Optional[int] = None, poison: bool = True,
-                  rng: Optional[np.random.Generator] = None) -> Workload:
-    """Draw one decode batch.  ``seqlens`` counts the new tokens (each >= s_q)."""
+                  rng: Optional[np.random.Generator] = None, shape_values=None) -> Workload:
+    """Draw one decode batch.  ``seqlens`` counts the new tokens (each >= s_q).
+
+    ``shape_values(q, latent, rope, block_table, seqlens, rng)``, if given, may
+    rewrite the float32 draws in place before they are encoded (structured
+    inputs for a test).
+    """
     rng = np.random.default_rng(seed) if rng is None else rng
     seqlens = np.asarray(seqlens, dtype=np.int32)
     assert seqlens.shape == (batch,) and (seqlens >= s_q).all()
@@ -131,6 +136,8 @@ def make_workload(name: str, *, batch: int, num_heads: int, seqlens: Sequence[in
     rope = _normal_f32(rng, (P, PAGE, D_ROPE))
     if rope_std != 1.0:
         rope *= np.float32(rope_std)
+    if shape_values is not None:
+        shape_values(q, latent, rope, block_table, seqlens, rng)
     q_bits = f32_to_bf16_bits(q)
     del q
 
@@ -170,6 +177,36 @@ def make_workload(name: str, *, batch: int, num_heads: int, seqlens: Sequence[in
             kv_scale[~referenced] = np.nan
     return Workload(name=name, q=q_bits, cache=cache, kv_scale=kv_scale, block_table=block_table, seqlens=seqlens,
                     s_q=s_q, num_heads=num_heads, causal=causal)
+
+
+def make_score_jump_workload(name: str, *, seqlens: Sequence[int], jumps: Sequence[Sequence[tuple]],
+                             num_heads: int = 128, kv_dtype: str = "bf16", seed: int = 0,
+                             rope_high: float = 0.7) -> Workload:
+    """A batch whose scores jump: most keys give every head a score near 0, and a
+    few tokens per request (``jumps[b]`` = list of (first, count, level)) score
+    about 6.5 * level nats higher (a RoPE-part key of rope_high * level against a
+    query RoPE part of 2).  Low and high tokens carry latents with different
+    dim-dependent means, so each group's share of the softmax shows in the output.
+    """
+    def shape(q, latent, rope, block_table, sl, rng):
+        q[..., :D_LATENT] *= np.float32(0.05)
+        q[..., D_LATENT:] = np.float32(2.0) + np.float32(0.05) * q[..., D_LATENT:]
+        dims = np.arange(D_LATENT, dtype=np.float32)
+        low_mean = np.sin(np.float32(0.05) * dims).astype(np.float32)
+        high_mean = -np.cos(np.float32(0.11) * dims).astype(np.float32)
+        latent *= np.float32(0.3)
+        latent += low_mean
+        rope *= np.float32(0.05)
+        for b, spans in enumerate(jumps):
+            for first, count, level in spans:
+                for t in range(first, first + count):
+                    assert t < sl[b]
+                    page, slot = block_table[b, t // PAGE], t % PAGE
+                    latent[page, slot] += high_mean - low_mean
+                    rope[page, slot] += np.float32(rope_high * level)
+
+    return make_workload(name, batch=len(seqlens), num_heads=num_heads, seqlens=seqlens, seed=seed,
+                         kv_dtype=kv_dtype, spare_pages=2, shape_values=shape)
 
 
 def ragged_seqlens(rng: np.random.Generator, batch: int, lo: int = 128, hi: int = 32768) -> np.ndarray:
