@@ -16,7 +16,10 @@
 // compute problem" section -- heads as the M dimension, the latent as K, one
 // block handling all heads and a stretch of KV.
 //   * Pages stream HBM -> LDS with direct-to-LDS loads (no VGPR staging) into a
-//     ring of 4 slots of 32 tokens (4 x 36 KiB), three slots in flight.
+//     ring of 4 slots of 32 tokens (4 x 36 KiB), three slots in flight.  A
+//     chunk's page comes from a block-table window held one entry per lane
+//     (a readlane, no scalar load to wait on), and each wave's loads of a
+//     chunk go out from one asm block with precomputed per-lane offsets.
 //   * Each wave holds its 16 rows of q~ in registers (18 MFMA B-fragments) and
 //     computes S^T = KV . q~^T with v_mfma_f32_16x16x32_bf16: tokens are M and
 //     rows are N, so every lane owns one row and the softmax statistics need two
@@ -28,7 +31,13 @@
 //     so one wave's softmax overlaps the other's MFMAs, and each wave fits in
 //     256 registers (q~ 72, O 128, scores 8, the rest working set).
 //   * The running maximum is rescaled lazily: O and the normaliser are only
-//     rescaled when a new maximum exceeds the reference by more than 2^8.
+//     rescaled when a new maximum exceeds the reference by more than 2^8.  The
+//     test is on each lane's own maximum (one ballot); the cross-lane row
+//     maximum is formed only when it fires.  The scale is folded into the
+//     exponent's FMA.
+//   * The LDS reads of the two contractions are pinned one (scores) and two
+//     (values) MFMAs ahead with scheduling barriers: without them the compiler
+//     sinks each read to its use and every MFMA waits a full LDS latency.
 //   * Tokens past the request's length are never loaded (their rows are
 //     replaced by the last valid token) and are masked to -inf, so stale or NaN
 //     bytes in a partly used last page cannot reach the output.
@@ -110,18 +119,50 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t 
 // Direct-to-LDS loads this wave issues per slot: 36 one-KiB blocks over 8 waves.
 __device__ __forceinline__ int dma_per_slot(int wave) { return wave < kSlotBlocks - 4 * kWaves ? 5 : 4; }
 
-// Fill part i of one LDS slot with 32 consecutive token rows starting at src
-// (all in one page).  LDS granule blk*64 + lane is row tok, physical granule
-// phys, which holds logical granule phys ^ swz(tok).  Rows at or past `valid`
-// repeat row valid-1, so bytes past a request's end are never read.
-__device__ __forceinline__ void load_chunk_part(const char* src, int valid, uint32_t slot_lds, int i, int wave,
-                                                int lane) {
-  const int blk = i * kWaves + wave;    // 1 KiB block of the slot this instruction fills
-  const int gi = blk * 64 + lane;       // granule index within the slot
+// Source offset of load i of this lane: LDS granule (i*8 + wave)*64 + lane of a
+// slot is row tok = g / 72, physical granule g % 72, which holds logical granule
+// (g % 72) ^ swz(tok).  Rows at or past `valid` repeat row valid-1, so bytes past
+// a request's end are never read.
+__device__ __forceinline__ int dma_off(int i, int wave, int lane, int valid) {
+  const int gi = (i * kWaves + wave) * 64 + lane;
   const int tok = gi / kGranPerRow;
   const int phys = gi - tok * kGranPerRow;
   const int src_tok = tok < valid ? tok : valid - 1;
-  dma16(src, (uint32_t)(src_tok * kRowBytes + ((phys ^ swz(tok)) << 4)), slot_lds + blk * 1024);
+  return src_tok * kRowBytes + ((phys ^ swz(tok)) << 4);
+}
+
+// All of this wave's direct-to-LDS loads of one chunk in one asm block: load i
+// reads base + voff[i] into the 1 KiB LDS block m0 + 8192 i (block i*8 + wave).
+// The wait states cover an SGPR base just written by VALU (5) and each M0
+// update (1).  Waves 0-3 issue five loads, waves 4-7 four.
+__device__ __forceinline__ void dma_chunk(const void* base, uint32_t m0, const int (&voff)[5], bool five) {
+  const uint64_t b = (uint64_t)base;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+  const uint64_t sbase = ((uint64_t)hi << 32) | (uint64_t)lo;
+  uint32_t m = __builtin_amdgcn_readfirstlane(m0);
+  if (five) {
+    asm volatile(
+        "s_nop 4\n\t"
+        "global_load_lds_dwordx4 %1, %6\n\ts_add_u32 m0, m0, 8192\n\ts_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, %6\n\ts_add_u32 m0, m0, 8192\n\ts_nop 0\n\t"
+        "global_load_lds_dwordx4 %3, %6\n\ts_add_u32 m0, m0, 8192\n\ts_nop 0\n\t"
+        "global_load_lds_dwordx4 %4, %6\n\ts_add_u32 m0, m0, 8192\n\ts_nop 0\n\t"
+        "global_load_lds_dwordx4 %5, %6"
+        : "+{m0}"(m)
+        : "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "v"(voff[4]), "s"(sbase)
+        : "memory");
+  } else {
+    asm volatile(
+        "s_nop 4\n\t"
+        "global_load_lds_dwordx4 %1, %5\n\ts_add_u32 m0, m0, 8192\n\ts_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, %5\n\ts_add_u32 m0, m0, 8192\n\ts_nop 0\n\t"
+        "global_load_lds_dwordx4 %3, %5\n\ts_add_u32 m0, m0, 8192\n\ts_nop 0\n\t"
+        "global_load_lds_dwordx4 %4, %5"
+        : "+{m0}"(m)
+        : "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "s"(sbase)
+        : "memory");
+  }
 }
 
 // The lane index, hidden from the optimiser.  Per-lane address terms derived
@@ -185,6 +226,9 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
   const bool row_ok = row < a.rows;
   const int qi = row_ok ? row / a.num_heads : 0;   // which new token this row belongs to
   const int ndma = dma_per_slot(wave);
+  int voff_full[5];   // this lane's load offsets for a full chunk
+#pragma unroll
+  for (int i = 0; i < 5; i++) voff_full[i] = dma_off(i, wave, lane, kChunk);
 
   // Per-lane LDS byte offsets within a slot.
   // QK A-operand: token 16tt + n, logical granule 4k + q -> physical 8(k>>1) + ((4(k&1)) ^ y).
@@ -218,27 +262,47 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
     const int nchunks = (t_hi - t_lo + kChunk - 1) / kChunk;
     const int n_vis = a.causal ? L - a.seqlen_q + 1 + qi : L;      // keys this lane's row may see
     const int min_vis = a.causal ? L - a.seqlen_q + 1 : L;          // smallest over the request's rows
-    const int32_t CONST_AS* bt = (const int32_t CONST_AS*)(a.block_table + (size_t)b * a.max_blocks);
+    const int32_t* bt_row = a.block_table + (size_t)b * a.max_blocks;
     const char* kv = reinterpret_cast<const char*>(a.kv);
 
     // The previous segment's readers of the slots are done.
     __syncthreads();
 
+    // Block-table window: lane i holds the page of request page pg0 + win + i,
+    // so a chunk's page is one readlane rather than a scalar load waited on.
+    auto load_window = [&](int w) {
+      const int pi = pg0 + w + opaque_lane();
+      return pi < pg1 ? bt_row[pi] : 0;
+    };
+    int win = 0;
+    int win_pages = load_window(0);
+
     auto issue = [&](int c) {
       const int t0 = t_lo + c * kChunk;
-      int page = bt[t0 / kPageSize];
-      if (page < 0 || page >= a.num_pages) {
-        if (tid == 0) atomicOr(&hdr->flags, 2u);
-        page = 0;
+      int pw = (c >> 1) - win;   // t_lo is page aligned: two chunks per page
+      if (pw >= 64) {
+        win += 64;
+        pw -= 64;
+        win_pages = load_window(win);
       }
+      int page = __builtin_amdgcn_readlane(win_pages, pw);
+      const bool bad = page < 0 || page >= a.num_pages;
+      page = bad ? 0 : page;
+      if (bad && tid == 0) atomicOr(&hdr->flags, 2u);
       const char* src = kv + ((size_t)page * kPageSize + (t0 % kPageSize)) * kRowBytes;
       const int valid = t_hi - t0 < kChunk ? t_hi - t0 : kChunk;
-      const uint32_t slot_lds = smem_addr + (c % kSlots) * kSlotBytes;
+      const uint32_t m0 = smem_addr + (c % kSlots) * kSlotBytes + wave * 1024;
+      if (valid == kChunk) {
+        dma_chunk(src, m0, voff_full, ndma == 5);
+      } else {   // a request's last, partial chunk
+        const int l = opaque_lane();
+        int voff[5];
 #pragma unroll
-      for (int i = 0; i < 5; i++)
-        if (i < ndma) load_chunk_part(src, valid, slot_lds, i, wave, lane);
+        for (int i = 0; i < 5; i++) voff[i] = dma_off(i, wave, l, valid);
+        dma_chunk(src, m0, voff, ndma == 5);
+      }
     };
-    for (int c = 0; c < kSlots - 1 && c < nchunks; c++) issue(c);
+    issue(0);
 
     // Queries, loaded after the first page loads so that both latencies overlap;
     // one wait covers them all (the compiler tracks only the query loads).
@@ -255,6 +319,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
       }
     }
     __builtin_amdgcn_s_waitcnt(VMCNT(0));
+    for (int c = 1; c < kSlots - 1 && c < nchunks; c++) issue(c);
 
     float m_ref = -INFINITY;   // reference maximum (log2 units), same in all lanes of a row
     float lsum = 0.f;          // this lane's part of the normaliser
@@ -297,23 +362,30 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
         s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[k], s1, 0, 0, 0);
         a0 = n0;
         a1 = n1;
+        // keep step k+1's reads ahead of step k's MFMAs
+        __builtin_amdgcn_sched_barrier(0);
       }
 
-      // Scale, mask, online softmax.  s0[i] is token 4q + i, s1[i] token 16 + 4q + i.
-      float v[8];
-      float cmax = -INFINITY;
-      const bool need_mask = t0 + kChunk > min_vis;
+      // Mask, online softmax.  s0[i] is token 4q + i, s1[i] token 16 + 4q + i.
+      // Keys at or past the row's visible length are set to -inf; only a
+      // request's last chunk, or its causal tail, needs it (uniform branch).
+      if (t0 + kChunk > min_vis) {
+        const int lim = n_vis - t0 - 4 * q;   // token 4q + i visible if i < lim, 16 + 4q + i if 16 + i < lim
 #pragma unroll
-      for (int i = 0; i < 8; i++) {
-        float x = (i < 4 ? s0[i] : s1[i - 4]) * a.scale_log2;
-        if (need_mask && t0 + 16 * (i >> 2) + 4 * q + (i & 3) >= n_vis) x = -INFINITY;
-        v[i] = x;
-        cmax = fmaxf(cmax, x);
+        for (int i = 0; i < 4; i++) {
+          if (i >= lim) s0[i] = -INFINITY;
+          if (16 + i >= lim) s1[i] = -INFINITY;
+        }
       }
-      cmax = row_max(cmax);
-      const bool need = cmax > m_ref + kLazyRescale;
-      if (__builtin_amdgcn_ballot_w64(need)) {
-        const float m_new = need ? cmax : m_ref;
+      // This lane's maximum over its 8 scores (the scale is positive, so it is
+      // applied to the maximum).  Lazy rescale: nothing to do unless some score
+      // exceeds the row's reference by more than 2^8; only then is the exact
+      // row maximum formed and taken as the new reference.
+      float cmax = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
+                         fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3]))) * a.scale_log2;
+      if (__builtin_amdgcn_ballot_w64(cmax > m_ref + kLazyRescale)) {
+        const float rmax = row_max(cmax);
+        const float m_new = rmax > m_ref + kLazyRescale ? rmax : m_ref;
         const float alpha = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
         lsum *= alpha;
 #pragma unroll
@@ -324,7 +396,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
       bf16x8_t pb;
 #pragma unroll
       for (int i = 0; i < 8; i++) {
-        const float p = __builtin_amdgcn_exp2f(v[i] - mu);
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(i < 4 ? s0[i] : s1[i - 4], a.scale_log2, -mu));
         lsum += p;
         pb[i] = (__bf16)p;
       }
@@ -345,6 +417,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
         o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v0, pb, o[d], 0, 0, 0);
         v0 = v1;
         v1 = v2;
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
 
