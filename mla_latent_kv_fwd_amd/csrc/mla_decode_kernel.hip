@@ -582,15 +582,29 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_fp8_kernel(DecodeArgs 
     const int nchunks = (t_hi - t_lo + kChunk8 - 1) / kChunk8;
     const int n_vis = a.causal ? L - a.seqlen_q + 1 + qi : L;
     const int min_vis = a.causal ? L - a.seqlen_q + 1 : L;
-    const int32_t CONST_AS* bt = (const int32_t CONST_AS*)(a.block_table + (size_t)b * a.max_blocks);
+    const int32_t* bt_row = a.block_table + (size_t)b * a.max_blocks;
     const char* kv = reinterpret_cast<const char*>(a.kv);
 
     // The previous segment's readers of the slots are done.
     __syncthreads();
 
+    // Block-table window (see the bf16 kernel).
+    auto load_window = [&](int w) {
+      const int pi = pg0 + w + opaque_lane();
+      return pi < pg1 ? bt_row[pi] : 0;
+    };
+    int win = 0;
+    int win_pages = load_window(0);
+
     auto issue = [&](int c) {
       const int t0 = t_lo + c * kChunk8;
-      int page = bt[t0 / kPageSize];
+      int pw = (c >> 1) - win;   // t_lo is page aligned: two chunks per page
+      if (pw >= 64) {
+        win += 64;
+        pw -= 64;
+        win_pages = load_window(win);
+      }
+      int page = __builtin_amdgcn_readlane(win_pages, pw);
       const bool bad = page < 0 || page >= a.num_pages;
       page = bad ? 0 : page;
       if (bad && tid == 0) atomicOr(&hdr->flags, 2u);
@@ -605,7 +619,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_fp8_kernel(DecodeArgs 
           load_chunk_part8(src, ssrc, valid, smem_addr + slot * kSlotBytes8, scale_addr + slot * kScaleBytes8, i,
                            wave, lane);
     };
-    for (int c = 0; c < kSlots8 - 1 && c < nchunks; c++) issue(c);
+    issue(0);
 
     // Queries, loaded after the first page loads so that both latencies overlap;
     // one wait covers them all (the compiler tracks only the query loads).
@@ -625,6 +639,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_fp8_kernel(DecodeArgs 
         }
     }
     __builtin_amdgcn_s_waitcnt(VMCNT(0));
+    // Later chunks land while chunk 0 is processed.
+    for (int c = 1; c < kSlots8 - 1 && c < nchunks; c++) issue(c);
 
     float m_ref = -INFINITY;
     float lsum = 0.f;
@@ -688,21 +704,30 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_fp8_kernel(DecodeArgs 
       // Token scales of this lane's eight tokens: 4q + i and 16 + 4q + i.
       const f32x4_t sc0 = *reinterpret_cast<const f32x4_t LDS_AS*>(sc_lds + 4 * q);
       const f32x4_t sc1 = *reinterpret_cast<const f32x4_t LDS_AS*>(sc_lds + 16 + 4 * q);
-      float v[8];
-      float cmax = -INFINITY;
-      const bool need_mask = t0 + kChunk8 > min_vis;
+      float x[8], w[8];   // scaled scores (before the softmax scale) and p's token scale
 #pragma unroll
       for (int i = 0; i < 8; i++) {
-        const float sc = i < 4 ? sc0[i] : sc1[i - 4];
-        float x = (i < 4 ? s0[i] : s1[i - 4]) * sc * a.scale_log2;
-        if (need_mask && t0 + 16 * (i >> 2) + 4 * q + (i & 3) >= n_vis) x = -INFINITY;
-        v[i] = x;
-        cmax = fmaxf(cmax, x);
+        w[i] = i < 4 ? sc0[i] : sc1[i - 4];
+        x[i] = (i < 4 ? s0[i] : s1[i - 4]) * w[i];
       }
-      cmax = row_max(cmax);
-      const bool need = cmax > m_ref + kLazyRescale;
-      if (__builtin_amdgcn_ballot_w64(need)) {
-        const float m_new = need ? cmax : m_ref;
+      // Keys at or past the row's visible length (a request's last chunk or
+      // causal tail, a uniform branch) get score -inf and weight scale 0: a
+      // scale past a request's end may be anything, NaN included.
+      if (t0 + kChunk8 > min_vis) {
+        const int lim = n_vis - t0 - 4 * q;
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+          if (16 * (i >> 2) + (i & 3) >= lim) {
+            x[i] = -INFINITY;
+            w[i] = 0.f;
+          }
+      }
+      // Lazy rescale tested on this lane's own maximum (see the bf16 kernel).
+      float cmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7]))) *
+                   a.scale_log2;
+      if (__builtin_amdgcn_ballot_w64(cmax > m_ref + kLazyRescale)) {
+        const float rmax = row_max(cmax);
+        const float m_new = rmax > m_ref + kLazyRescale ? rmax : m_ref;
         const float alpha = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
         lsum *= alpha;
 #pragma unroll
@@ -713,11 +738,9 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_fp8_kernel(DecodeArgs 
       bf16x8_t pb;
 #pragma unroll
       for (int i = 0; i < 8; i++) {
-        const float p = __builtin_amdgcn_exp2f(v[i] - mu);
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], a.scale_log2, -mu));
         lsum += p;
-        // a masked token's scale may be anything (past the request's end): keep its p at 0
-        const float sc = i < 4 ? sc0[i] : sc1[i - 4];
-        pb[i] = (__bf16)(v[i] == -INFINITY ? 0.f : p * sc);
+        pb[i] = (__bf16)(p * w[i]);
       }
 
       // O^T += V^T . P'^T: one transposing read of 8 tokens x 16 codes per tile.
