@@ -9,8 +9,8 @@
 // carries no weight and its output is not read.
 //
 // Memory-bound: one 512-wide fp32 row per piece in, one bf16 row out.  A
-// workgroup of 256 threads handles two rows; each thread owns four consecutive
-// output columns (16-byte loads, 8-byte stores).  The pieces are merged in one
+// workgroup of 256 threads handles four rows; each thread owns eight
+// consecutive output columns (two 16-byte loads per piece, two 8-byte stores).  The pieces are merged in one
 // online pass (running maximum, normaliser and weighted sum, rescaled when the
 // maximum grows), so the LSEs and partial rows of a group of pieces are all
 // loaded before any of them is used: one memory latency per group instead of
@@ -32,25 +32,28 @@ typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 #define CONST_AS __attribute__((address_space(4)))
 
 constexpr int kThreads = 256;
-constexpr int kRowsPerWg = 2;
-constexpr int kThreadsPerRow = kThreads / kRowsPerWg;   // 128 threads x 4 columns = 512
+constexpr int kCols = 8;                                // output columns per thread
+constexpr int kThreadsPerRow = kHeadDimV / kCols;       // 64
+constexpr int kRowsPerWg = kThreads / kThreadsPerRow;   // 4
 constexpr int kGroup = 4;                               // pieces loaded together
 
 __global__ __launch_bounds__(kThreads) void mla_combine_kernel(const char* __restrict__ ws, Layout lay, int rows,
                                                                uint16_t* __restrict__ out, float* __restrict__ lse) {
   const int b = blockIdx.x;
   const int row = blockIdx.y * kRowsPerWg + threadIdx.x / kThreadsPerRow;
-  const int col = (threadIdx.x % kThreadsPerRow) * 4;
+  const int col = (threadIdx.x % kThreadsPerRow) * kCols;
   if (row >= rows) return;
   // Request info is uniform over the workgroup: scalar loads.
   const int32_t CONST_AS* rqp = (const int32_t CONST_AS*)(ws + lay.req_info + sizeof(ReqInfo) * b);
   const int npages = rqp[offsetof(ReqInfo, npages) / 4], nsplit = rqp[offsetof(ReqInfo, nsplit) / 4],
             slot_off = rqp[offsetof(ReqInfo, slot_off) / 4];
   const size_t orow = (size_t)b * rows + row;
+  // out is 8-byte aligned: two 8-byte stores per thread.
   bf16x4_t* dst = reinterpret_cast<bf16x4_t*>(out + orow * kHeadDimV + col);
 
   if (npages == 0) {   // a request with no tokens: defined empty result
-    *dst = bf16x4_t{};
+    dst[0] = bf16x4_t{};
+    dst[1] = bf16x4_t{};
     if (col == 0) lse[orow] = -INFINITY;
     return;
   }
@@ -65,15 +68,17 @@ __global__ __launch_bounds__(kThreads) void mla_combine_kernel(const char* __res
   auto pidx = [&](int j) { return ((size_t)(slot_off + j) * nrb + rb) * kRowsPerBlock + rr; };
 
   float m = -INFINITY, z = 0.f;
-  f32x4_t acc = f32x4_t{};
+  f32x4_t acc0 = f32x4_t{}, acc1 = f32x4_t{};
   for (int j0 = 0; j0 < nsplit; j0 += kGroup) {
     float lj[kGroup];
-    f32x4_t oj[kGroup];
+    f32x4_t oj0[kGroup], oj1[kGroup];
 #pragma unroll
     for (int g = 0; g < kGroup; g++) {
       const bool ok = j0 + g < nsplit;
       lj[g] = ok ? plse[pidx(j0 + g)] : -INFINITY;
-      oj[g] = ok ? *reinterpret_cast<const f32x4_t*>(pout + pidx(j0 + g) * kHeadDimV + col) : f32x4_t{};
+      const f32x4_t* src = reinterpret_cast<const f32x4_t*>(pout + pidx(j0 + g) * kHeadDimV + col);
+      oj0[g] = ok ? src[0] : f32x4_t{};
+      oj1[g] = ok ? src[1] : f32x4_t{};
     }
 #pragma unroll
     for (int g = 0; g < kGroup; g++) {
@@ -82,20 +87,26 @@ __global__ __launch_bounds__(kThreads) void mla_combine_kernel(const char* __res
       const float keep = __expf(m - m2);  // 0 while m is still -inf
       const float w = __expf(lj[g] - m2);
       z = z * keep + w;
-      acc = acc * keep + w * oj[g];
+      acc0 = acc0 * keep + w * oj0[g];
+      acc1 = acc1 * keep + w * oj1[g];
       m = m2;
     }
   }
   if (m == -INFINITY) {
-    *dst = bf16x4_t{};
+    dst[0] = bf16x4_t{};
+    dst[1] = bf16x4_t{};
     if (col == 0) lse[orow] = -INFINITY;
     return;
   }
   const float inv = 1.f / z;
-  bf16x4_t r;
+  bf16x4_t r0, r1;
 #pragma unroll
-  for (int i = 0; i < 4; i++) r[i] = (__bf16)(acc[i] * inv);
-  *dst = r;
+  for (int i = 0; i < 4; i++) {
+    r0[i] = (__bf16)(acc0[i] * inv);
+    r1[i] = (__bf16)(acc1[i] * inv);
+  }
+  dst[0] = r0;
+  dst[1] = r1;
   if (col == 0) lse[orow] = m + __logf(z);
 }
 

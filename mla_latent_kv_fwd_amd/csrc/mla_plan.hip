@@ -11,7 +11,7 @@
 // handles) and the FlashMLA guide's "Native Ragged Sequence Batching" (work
 // assigned by context length so long and short requests share the GPU).
 //
-// One workgroup of 1024 threads does the whole plan on the device from the
+// One workgroup of 256 threads does the whole plan on the device from the
 // device-resident sequence lengths, so no host synchronisation is needed.  All
 // working arrays live in LDS (batch <= kMaxBatch, stretches <= kMaxStretches),
 // so every binary search is a handful of LDS reads.
@@ -24,34 +24,44 @@
 namespace mla {
 namespace {
 
-constexpr int kPlanThreads = 1024;
+constexpr int kPlanThreads = 256;
 constexpr int kPlanWaves = kPlanThreads / 64;
 
 // Inclusive scan over the workgroup; `wsum` is scratch for the per-wave totals.
 // Returns the inclusive prefix of this thread; *total receives the block total.
-__device__ int block_scan(int v, int* wsum, int* total) {
+// Two independent values are scanned together (one set of barriers).
+__device__ int2 block_scan2(int2 v, int2* wsum, int2* total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(v, off, 64);
-    if (lane >= off) v += y;
+    const int yx = __shfl_up(v.x, off, 64), yy = __shfl_up(v.y, off, 64);
+    if (lane >= off) {
+      v.x += yx;
+      v.y += yy;
+    }
   }
   if (lane == 63) wsum[w] = v;
   __syncthreads();
-  if (w == 0) {
-    int s = lane < kPlanWaves ? wsum[lane] : 0;
+  int2 pre = make_int2(0, 0), tot = make_int2(0, 0);
 #pragma unroll
-    for (int off = 1; off < kPlanWaves; off <<= 1) {
-      const int y = __shfl_up(s, off, 64);
-      if (lane >= off) s += y;
+  for (int i = 0; i < kPlanWaves; i++) {   // a handful of waves: read the totals directly
+    const int2 x = wsum[i];
+    if (i < w) {
+      pre.x += x.x;
+      pre.y += x.y;
     }
-    if (lane < kPlanWaves) wsum[lane] = s;
+    tot.x += x.x;
+    tot.y += x.y;
   }
+  *total = tot;
   __syncthreads();
-  const int r = v + (w > 0 ? wsum[w - 1] : 0);
-  *total = wsum[kPlanWaves - 1];
-  __syncthreads();
-  return r;
+  return make_int2(v.x + pre.x, v.y + pre.y);
+}
+__device__ int block_scan(int v, int2* wsum, int* total) {
+  int2 t;
+  const int2 r = block_scan2(make_int2(v, 0), wsum, &t);
+  *total = t.x;
+  return r.x;
 }
 
 // Largest index i in [0, n) with key(i) <= x, or -1.
@@ -73,7 +83,7 @@ __global__ __launch_bounds__(kPlanThreads) void mla_plan_kernel(const int32_t* _
   __shared__ int s_np[kMaxBatch];         // pages of each request
   __shared__ int s_bnd[kMaxStretches + 1];   // stretch boundaries in page positions
   __shared__ int s_ne[kMaxStretches + 1];    // non-empty stretches before each stretch
-  __shared__ int wsum[kPlanWaves];
+  __shared__ int2 wsum[kPlanWaves];
   __shared__ unsigned flags;
 
   Header* hdr = reinterpret_cast<Header*>(ws + lay.header);
@@ -96,9 +106,9 @@ __global__ __launch_bounds__(kPlanThreads) void mla_plan_kernel(const int32_t* _
     }
     const int np = (L + kPageSize - 1) / kPageSize;
     const int cost = np > 0 ? np + kPlanCostPerRequest : 0;
-    int tot_p, tot_c;
-    const int inc_p = block_scan(np, wsum, &tot_p);
-    const int inc_c = block_scan(cost, wsum, &tot_c);
+    int2 tot;
+    const int2 inc = block_scan2(make_int2(np, cost), wsum, &tot);
+    const int inc_p = inc.x, inc_c = inc.y, tot_p = tot.x, tot_c = tot.y;
     if (b < batch) {
       s_first[b] = carry_p + inc_p - np;
       s_np[b] = np;
