@@ -4,9 +4,11 @@ Argument marshalling only.  Every step of the decode runs in the HIP kernels of
 the shared library; this module never computes attention itself, and it raises
 if the library is missing.  PyTorch supplies device memory and streams.
 
-The entry points carry the names of the C ABI (include/mla_decode.h):
-``mla_get_workspace``, ``mla_decode_fwd``, ``mla_splitkv_combine``,
-``mla_workspace_flags``.  ``MlaDecode`` wraps them for torch tensors.
+The entry points carry the names of the C ABI (include/mla_decode.h,
+include/mla_proj.h): ``mla_get_workspace``, ``mla_decode_fwd``,
+``mla_splitkv_combine``, ``mla_workspace_flags``, ``mla_absorb_q``,
+``mla_project_out``.  ``MlaDecode`` wraps the decode step for torch tensors;
+``absorb_q`` and ``project_out`` the two projections.
 """
 from __future__ import annotations
 
@@ -33,7 +35,8 @@ PAGE_SIZE = 64
 SOFTMAX_SCALE = 1.0 / math.sqrt(128 + 64)
 
 EXPORTED_SYMBOLS = ("mla_get_workspace", "mla_decode_fwd", "mla_splitkv_combine", "mla_workspace_flags",
-                    "mla_status_string")
+                    "mla_status_string", "mla_absorb_q", "mla_project_out")
+D_NOPE, D_ROPE, D_LATENT, D_V = 128, 64, 512, 128
 
 
 class MlaError(RuntimeError):
@@ -48,6 +51,16 @@ class DecodeParams(ctypes.Structure):
                 ("head_dim_qk", ctypes.c_int32), ("head_dim_v", ctypes.c_int32), ("page_size", ctypes.c_int32),
                 ("num_pages", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
                 ("causal", ctypes.c_int32), ("softmax_scale", ctypes.c_float), ("num_workgroups", ctypes.c_int32)]
+
+
+class ProjParams(ctypes.Structure):
+    """Mirror of mla_proj_params."""
+    _fields_ = [("tokens", ctypes.c_int32), ("num_heads", ctypes.c_int32), ("d_nope", ctypes.c_int32),
+                ("d_rope", ctypes.c_int32), ("d_latent", ctypes.c_int32), ("d_v", ctypes.c_int32)]
+
+
+def make_proj_params(*, tokens, num_heads, d_nope=D_NOPE, d_rope=D_ROPE, d_latent=D_LATENT, d_v=D_V) -> ProjParams:
+    return ProjParams(tokens, num_heads, d_nope, d_rope, d_latent, d_v)
 
 
 def make_params(*, batch, seqlen_q, num_heads, num_pages, max_blocks_per_seq, kv_dtype=MLA_KV_BF16, causal=False,
@@ -76,7 +89,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_workspace_flags.argtypes = [vp, ctypes.POINTER(ctypes.c_uint32), vp]
     lib.mla_status_string.argtypes = [ctypes.c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
-    for name in ("mla_get_workspace", "mla_decode_fwd", "mla_splitkv_combine", "mla_workspace_flags"):
+    ppp = ctypes.POINTER(ProjParams)
+    lib.mla_absorb_q.argtypes = [ppp, vp, vp, vp, vp, vp]
+    lib.mla_project_out.argtypes = [ppp, vp, vp, vp, vp]
+    for name in ("mla_get_workspace", "mla_decode_fwd", "mla_splitkv_combine", "mla_workspace_flags", "mla_absorb_q",
+                 "mla_project_out"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -117,6 +134,52 @@ def mla_workspace_flags(workspace_ptr: int, stream: int = 0) -> int:
     _check("mla_workspace_flags", load_library().mla_workspace_flags(workspace_ptr or None, ctypes.byref(flags),
                                                                      stream or None))
     return flags.value
+
+
+def mla_absorb_q(params: ProjParams, q_nope_ptr: int, q_rope_ptr: int, w_uk_ptr: int, q_tilde_ptr: int,
+                 stream: int = 0) -> None:
+    _check("mla_absorb_q", load_library().mla_absorb_q(
+        ctypes.byref(params), q_nope_ptr or None, q_rope_ptr or None, w_uk_ptr or None, q_tilde_ptr or None,
+        stream or None))
+
+
+def mla_project_out(params: ProjParams, o_latent_ptr: int, w_uv_ptr: int, out_ptr: int, stream: int = 0) -> None:
+    _check("mla_project_out", load_library().mla_project_out(
+        ctypes.byref(params), o_latent_ptr or None, w_uv_ptr or None, out_ptr or None, stream or None))
+
+
+def _bf16_tensor(x, shape, name):
+    if tuple(x.shape) != tuple(shape) or x.element_size() != 2 or not x.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous 16-bit tensor of shape {tuple(shape)}, got {tuple(x.shape)}")
+
+
+def absorb_q(q_nope, q_rope, w_uk, out=None):
+    """q~ [T, H, 576] bf16 from q^N [T, H, 128], q^R [T, H, 64] and W_UK [H, 128, 512] (all bf16 on the device)."""
+    import torch
+    T, H = q_nope.shape[0], q_nope.shape[1]
+    _bf16_tensor(q_nope, (T, H, D_NOPE), "q_nope")
+    _bf16_tensor(q_rope, (T, H, D_ROPE), "q_rope")
+    _bf16_tensor(w_uk, (H, D_NOPE, D_LATENT), "w_uk")
+    if out is None:
+        out = torch.empty((T, H, D_LATENT + D_ROPE), dtype=q_nope.dtype, device=q_nope.device)
+    _bf16_tensor(out, (T, H, D_LATENT + D_ROPE), "out")
+    mla_absorb_q(make_proj_params(tokens=T, num_heads=H), q_nope.data_ptr(), q_rope.data_ptr(), w_uk.data_ptr(),
+                 out.data_ptr(), torch.cuda.current_stream(q_nope.device).cuda_stream)
+    return out
+
+
+def project_out(o_latent, w_uv, out=None):
+    """W_UV[h] o[t,h]: [T, H, 128] bf16 from o [T, H, 512] and W_UV [H, 128, 512] (all bf16 on the device)."""
+    import torch
+    T, H = o_latent.shape[0], o_latent.shape[1]
+    _bf16_tensor(o_latent, (T, H, D_LATENT), "o_latent")
+    _bf16_tensor(w_uv, (H, D_V, D_LATENT), "w_uv")
+    if out is None:
+        out = torch.empty((T, H, D_V), dtype=o_latent.dtype, device=o_latent.device)
+    _bf16_tensor(out, (T, H, D_V), "out")
+    mla_project_out(make_proj_params(tokens=T, num_heads=H), o_latent.data_ptr(), w_uv.data_ptr(), out.data_ptr(),
+                    torch.cuda.current_stream(o_latent.device).cuda_stream)
+    return out
 
 
 class MlaDecode:

@@ -1,4 +1,5 @@
-// mla_api.hip -- the C ABI of libmla_decode.so (declared in include/mla_decode.h):
+// mla_api.hip -- the C ABI of libmla_decode.so (declared in include/mla_decode.h
+// and include/mla_proj.h):
 // argument validation, workspace sizing and kernel launches.  No device memory
 // is allocated here; the caller owns every buffer.
 #include <hip/hip_runtime.h>
@@ -8,6 +9,7 @@
 
 #define MLA_HD __host__ __device__
 #include "mla_decode.h"
+#include "mla_proj.h"
 #include "mla_launch.h"
 #include "mla_workspace.h"
 
@@ -65,6 +67,18 @@ int resolve_nwg(const mla_decode_params* p, int* nwg) {
   *nwg = (int)(v < 1 ? 1 : v);
   return MLA_OK;
 }
+
+constexpr int kMaxProjTokens = 65536;
+
+int validate_proj(const mla_proj_params* p) {
+  if (!p) return MLA_ERR_INVALID_ARG;
+  if (p->tokens < 1 || p->tokens > kMaxProjTokens || p->num_heads < 1) return MLA_ERR_INVALID_ARG;
+  if (p->num_heads > kMaxHeads) return MLA_ERR_UNSUPPORTED;
+  if (p->d_nope != 128 || p->d_rope != 64 || p->d_latent != 512 || p->d_v != 128) return MLA_ERR_UNSUPPORTED;
+  return MLA_OK;
+}
+
+bool misaligned16(const void* ptr) { return ((uintptr_t)ptr & 15) != 0; }
 
 }  // namespace
 
@@ -153,6 +167,31 @@ int mla_splitkv_combine(const mla_decode_params* p, const void* workspace, size_
   if (workspace_bytes < lay.total) return MLA_ERR_WORKSPACE_TOO_SMALL;
   if (launch_combine(static_cast<const char*>(workspace), lay, p->batch, rows, static_cast<uint16_t*>(out), lse,
                      (hipStream_t)stream) != hipSuccess)
+    return MLA_ERR_HIP;
+  return MLA_OK;
+}
+
+int mla_absorb_q(const mla_proj_params* p, const void* q_nope, const void* q_rope, const void* w_uk, void* q_tilde,
+                 void* stream) {
+  const int st = validate_proj(p);
+  if (st != MLA_OK) return st;
+  if (!q_nope || !q_rope || !w_uk || !q_tilde) return MLA_ERR_INVALID_ARG;
+  if (misaligned16(q_nope) || misaligned16(q_rope) || misaligned16(w_uk) || misaligned16(q_tilde))
+    return MLA_ERR_INVALID_ARG;
+  if (launch_absorb_q(static_cast<const uint16_t*>(q_nope), static_cast<const uint16_t*>(q_rope),
+                      static_cast<const uint16_t*>(w_uk), static_cast<uint16_t*>(q_tilde), p->tokens, p->num_heads,
+                      (hipStream_t)stream) != hipSuccess)
+    return MLA_ERR_HIP;
+  return MLA_OK;
+}
+
+int mla_project_out(const mla_proj_params* p, const void* o_latent, const void* w_uv, void* out, void* stream) {
+  const int st = validate_proj(p);
+  if (st != MLA_OK) return st;
+  if (!o_latent || !w_uv || !out) return MLA_ERR_INVALID_ARG;
+  if (misaligned16(o_latent) || misaligned16(w_uv) || misaligned16(out)) return MLA_ERR_INVALID_ARG;
+  if (launch_project_out(static_cast<const uint16_t*>(o_latent), static_cast<const uint16_t*>(w_uv),
+                         static_cast<uint16_t*>(out), p->tokens, p->num_heads, (hipStream_t)stream) != hipSuccess)
     return MLA_ERR_HIP;
   return MLA_OK;
 }

@@ -161,6 +161,28 @@ def lse_merge(out_parts, lse_parts):
     return out, lse
 
 
+def absorb_q(q_nope, q_rope, w_uk):
+    """Absorbed query in float64: q~[t,h] = [W_UK[h]^T q^N[t,h] ; q^R[t,h]].
+
+    q_nope [T, H, dn], q_rope [T, H, dr], w_uk [H, dn, d_latent] (k^N = W_UK[h] c).
+    ("MLA inference: two computation paths and FlashMLA", section "Two
+    equivalent paths", path two: W_UK folded into the query.)  Returns
+    [T, H, d_latent + dr], latent part first.
+    """
+    q_lat = np.einsum("thn,hnc->thc", np.asarray(q_nope, np.float64), np.asarray(w_uk, np.float64))
+    return np.concatenate([q_lat, np.asarray(q_rope, np.float64)], axis=-1)
+
+
+def project_out(o_latent, w_uv):
+    """Output projection in float64: out[t,h] = W_UV[h] o[t,h].
+
+    o_latent [T, H, d_latent] (the latent-space attention output), w_uv
+    [H, dv, d_latent] (v = W_UV[h] c).  (Same passage: W_UV applied after the
+    attention.)  Returns [T, H, dv].
+    """
+    return np.einsum("thc,hvc->thv", np.asarray(o_latent, np.float64), np.asarray(w_uv, np.float64))
+
+
 def expand_attention(q_nope, q_rope, w_uk, w_uv, latent, k_rope, softmax_scale, query_pos, key_pos):
     """Expand path (path one) in float64, for one request.
 

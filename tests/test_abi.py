@@ -1,7 +1,8 @@
 """The C ABI boundary, checked without a GPU: the library loads, exports every
-function include/mla_decode.h declares, and rejects bad arguments with the
-documented status codes before anything is enqueued."""
+function include/*.h declares, and rejects bad arguments with the documented
+status codes before anything is enqueued."""
 import ctypes
+import glob
 import os
 import re
 
@@ -10,13 +11,15 @@ import pytest
 import mla_latent_kv_fwd_amd as M
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "mla_decode.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
 def _declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(mla_\w+)\s*\(", text, flags=re.M)))
+    names = set()
+    for header in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(header).read(), flags=re.S)
+        names |= set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(mla_\w+)\s*\(", text, flags=re.M))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -111,3 +114,35 @@ def test_missing_library_fails_loudly(tmp_path):
             M.load_library(str(tmp_path / "nope.so"))
         finally:
             M._lib = saved
+
+
+def _proj_params(**kw):
+    base = dict(tokens=64, num_heads=128)
+    base.update(kw)
+    return M.make_proj_params(**base)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("tokens", 0, M.MLA_ERR_INVALID_ARG),
+    ("tokens", 65537, M.MLA_ERR_INVALID_ARG),
+    ("num_heads", 0, M.MLA_ERR_INVALID_ARG),
+    ("num_heads", 129, M.MLA_ERR_UNSUPPORTED),
+    ("d_nope", 64, M.MLA_ERR_UNSUPPORTED),
+    ("d_rope", 32, M.MLA_ERR_UNSUPPORTED),
+    ("d_latent", 256, M.MLA_ERR_UNSUPPORTED),
+    ("d_v", 64, M.MLA_ERR_UNSUPPORTED),
+])
+def test_bad_projection_params_are_rejected(lib, field, value, status):
+    p = _proj_params()
+    setattr(p, field, value)
+    assert _status(lambda: M.mla_absorb_q(p, 16, 16, 16, 16)) == status
+    assert _status(lambda: M.mla_project_out(p, 16, 16, 16)) == status
+
+
+def test_projection_pointers_are_checked(lib):
+    p = _proj_params()
+    for args in ((0, 16, 16, 16), (16, 0, 16, 16), (16, 16, 0, 16), (16, 16, 16, 0), (24, 16, 16, 16),
+                 (16, 16, 16, 8)):
+        assert _status(lambda: M.mla_absorb_q(p, *args)) == M.MLA_ERR_INVALID_ARG, args
+    for args in ((0, 16, 16), (16, 0, 16), (16, 16, 0), (16, 32, 40)):
+        assert _status(lambda: M.mla_project_out(p, *args)) == M.MLA_ERR_INVALID_ARG, args

@@ -86,13 +86,13 @@ def _expand_vs_absorb(rng, H, T, s_q, causal, dc, dr, dn, dv, page=64):
     query_pos = np.arange(T - s_q, T) if causal else np.full(s_q, T - 1)
     out_exp, lse_exp = O.expand_attention(q_nope, q_rope, w_uk, w_uv, latent, rope, scale, query_pos, key_pos)
 
-    # absorb: q~ = [W_UK[h]^T q^N ; q^R], latent-space attention, then W_UV
-    q_lat = np.einsum("ihn,hnc->ihc", q_nope, w_uk)
-    q_tilde = np.concatenate([q_lat, q_rope], axis=-1)[None]          # [1, s_q, H, dc+dr]
+    # absorb: q~ = [W_UK[h]^T q^N ; q^R], latent-space attention, then W_UV (the
+    # oracle's absorb_q and project_out, so these pins cover them too)
+    q_tilde = O.absorb_q(q_nope, q_rope, w_uk)[None]                   # [1, s_q, H, dc+dr]
     cache, bt = _paged(latent, rope, rng, page=page)
     o_lat, lse_abs = O.attend(q_tilde, cache, bt, np.array([T], np.int32), softmax_scale=np.float32(scale),
                               causal=causal, d_rope=dr)
-    out_abs = np.einsum("ihc,hvc->ihv", o_lat[0], w_uv)
+    out_abs = O.project_out(o_lat[0], w_uv)
     # the oracle takes the scale as fp32; the expand path used the exact double.
     # Compare against an expand run at the same fp32-rounded scale:
     out_exp32, lse_exp32 = O.expand_attention(q_nope, q_rope, w_uk, w_uv, latent, rope,

@@ -238,3 +238,31 @@ def make_config(name: str, **overrides) -> Workload:
     else:
         seqlens = np.full(batch, seqlen, dtype=np.int32)
     return make_workload(name, seqlens=seqlens, rng=rng, **cfg)
+
+
+D_NOPE = 128
+D_V = 128
+
+
+@dataclasses.dataclass
+class ProjInputs:
+    q_nope: np.ndarray   # uint16 bf16 bits [T, H, 128]
+    q_rope: np.ndarray   # uint16 bf16 bits [T, H, 64]
+    w_uk: np.ndarray     # uint16 bf16 bits [H, 128, 512]   (k^N = W_UK[h] c)
+    w_uv: np.ndarray     # uint16 bf16 bits [H, 128, 512]   (v = W_UV[h] c)
+
+
+def make_proj_inputs(*, tokens: int, num_heads: int, seed: int = 0) -> ProjInputs:
+    """Per-head query parts and up-projection weights, bf16 bits.
+
+    q^N and q^R are standard normal; the weights are normal with std
+    1/sqrt(fan-in) (W_UK: 128, so an absorbed query number has variance ~1 like
+    the decode workloads' q; W_UV: 512).
+    """
+    rng = np.random.default_rng(seed)
+    q_nope = rng.standard_normal((tokens, num_heads, D_NOPE), dtype=np.float32)
+    q_rope = rng.standard_normal((tokens, num_heads, D_ROPE), dtype=np.float32)
+    w_uk = rng.standard_normal((num_heads, D_NOPE, D_LATENT), dtype=np.float32) * np.float32(1 / math.sqrt(D_NOPE))
+    w_uv = rng.standard_normal((num_heads, D_V, D_LATENT), dtype=np.float32) * np.float32(1 / math.sqrt(D_LATENT))
+    return ProjInputs(q_nope=f32_to_bf16_bits(q_nope), q_rope=f32_to_bf16_bits(q_rope), w_uk=f32_to_bf16_bits(w_uk),
+                      w_uv=f32_to_bf16_bits(w_uv))
