@@ -11,6 +11,8 @@ cannot be served from the 256 MB last-level cache (C is chosen so the copies
 total at least twice that, unless given).
 
 Prints one JSON line.  ``value`` is algorithmic TFLOP/s of the whole step;
+``projections`` times the two per-head projections on either side of the step
+(W_UK absorbed into the query, W_UV on the latent output) separately;
 ``roofline`` describes the attention kernel alone (its launches are timed with
 HIP events on the stream it runs on, inside the timed region; the plan and
 combine are timed in a separate pass because each event pair costs GPU time); ``cpu_baseline`` is the fp64 oracle run
@@ -83,6 +85,7 @@ def _parse():
     ap.add_argument("--copies", type=int, default=0, help="independent cache copies to cycle (0 = auto)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target duration of the CPU baseline sample")
+    ap.add_argument("--no-proj", action="store_true", help="skip the projection kernels' measurement")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB -> 1 GiB elementwise copy (calibrates the HBM byte counters)")
     return ap.parse_args()
@@ -132,6 +135,57 @@ def measured_traffic(workload, kv_dtype):
         return int(fields["decode_hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def projection_bytes(T, H):
+    """Algorithmic HBM bytes of one launch of each projection: weights, inputs and outputs once."""
+    w = H * D_NOPE * D_LATENT * 2
+    absorb = w + T * H * (D_NOPE + D_ROPE) * 2 + T * H * (D_LATENT + D_ROPE) * 2
+    project = w + T * H * D_LATENT * 2 + T * H * D_V * 2
+    return absorb, project
+
+
+def bench_projections(torch, M, W, T, H, launches=200):
+    """The two projections around the attention (W_UK absorbed into the query, W_UV on the latent output)
+    at this step's T = batch * s_q query rows: average time per launch over back-to-back launches between
+    one event pair, with weights, inputs and outputs cycled over copies that together exceed twice the
+    last-level cache."""
+    import numpy as np
+    b_abs, b_proj = projection_bytes(T, H)
+    nsets = max(2, math.ceil(2 * MALL_BYTES / (b_abs + b_proj)))
+    rng = np.random.default_rng(11)
+    pi = W.make_proj_inputs(tokens=T, num_heads=H, seed=10)
+    o_bits = W.f32_to_bf16_bits(rng.standard_normal((T, H, D_LATENT), dtype=np.float32) * np.float32(0.3))
+    dev = lambda b: torch.from_numpy(b.view(np.int16)).to("cuda")
+    base = [dev(pi.q_nope), dev(pi.q_rope), dev(pi.w_uk), dev(pi.w_uv), dev(o_bits)]
+    sets = []
+    for _ in range(nsets):
+        qn, qr, wuk, wuv, o = (x.clone() for x in base)
+        sets.append((qn, qr, wuk, wuv, o, torch.empty((T, H, D_LATENT + D_ROPE), dtype=torch.int16, device="cuda"),
+                     torch.empty((T, H, D_V), dtype=torch.int16, device="cuda")))
+    calls = {"absorb": lambda z: M.absorb_q(z[0], z[1], z[2], out=z[5]),
+             "project": lambda z: M.project_out(z[4], z[3], out=z[6])}
+    res = {}
+    for name, fn in calls.items():
+        for i in range(2 * nsets):
+            fn(sets[i % nsets])
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(launches):
+            fn(sets[i % nsets])
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) * 1e3 / launches
+    gbps = lambda nbytes, us: nbytes / (us * 1e-6) / 1e9
+    return {"tokens": T, "heads": H,
+            "absorb_q": {"us": round(res["absorb"], 3), "bytes": b_abs, "gbps": round(gbps(b_abs, res["absorb"]), 1),
+                         "frac_hbm": round(gbps(b_abs, res["absorb"]) / HBM_PEAK_GBPS, 4)},
+            "project_out": {"us": round(res["project"], 3), "bytes": b_proj,
+                            "gbps": round(gbps(b_proj, res["project"]), 1),
+                            "frac_hbm": round(gbps(b_proj, res["project"]) / HBM_PEAK_GBPS, 4)},
+            "timing": f"{launches} back-to-back launches between one event pair, {nsets} input/weight copies, "
+                      "after the timed region; not part of the step"}
 
 
 def cpu_baseline(wl, target_s):
@@ -260,6 +314,9 @@ def main():
         "roofline": roof,
         "flags": flags,
     }
+    if not args.no_proj:
+        del kvs, kss
+        line["projections"] = bench_projections(torch, M, W, wl.batch * wl.s_q, wl.num_heads)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(line), flush=True)
