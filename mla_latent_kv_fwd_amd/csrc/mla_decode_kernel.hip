@@ -18,8 +18,9 @@
 //   * Pages stream HBM -> LDS with direct-to-LDS loads (no VGPR staging) into a
 //     ring of 4 slots of 32 tokens (4 x 36 KiB), three slots in flight.  A
 //     chunk's page comes from a block-table window held one entry per lane
-//     (a readlane, no scalar load to wait on), and each wave's loads of a
-//     chunk go out from one asm block with precomputed per-lane offsets.
+//     (a readlane, no scalar load to wait on).  Waves 0-3 issue all of a
+//     chunk's loads, nine each, from one asm block with precomputed per-lane
+//     offsets; waves 4-7, which set the pace, issue none.
 //   * Each wave holds its 16 rows of q~ in registers (18 MFMA B-fragments) and
 //     computes S^T = KV . q~^T with v_mfma_f32_16x16x32_bf16: tokens are M and
 //     rows are N, so every lane owns one row and the softmax statistics need two
@@ -116,15 +117,21 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t 
                : "memory");
 }
 
-// Direct-to-LDS loads this wave issues per slot: 36 one-KiB blocks over 8 waves.
-__device__ __forceinline__ int dma_per_slot(int wave) { return wave < kSlotBlocks - 4 * kWaves ? 5 : 4; }
+// A slot is 36 one-KiB direct-to-LDS loads, all issued by waves 0-3 (nine
+// each).  On each SIMD the older wave (0-3) wins issue arbitration and then
+// waits at the chunk barrier for its sibling (4-7), so the load issue -- which
+// stalls while the CU's address unit drains the burst -- is moved off the
+// waves that set the pace.
+constexpr int kLoadWaves = 4;
+constexpr int kLoadsPerWave = kSlotBlocks / kLoadWaves;   // 9
+static_assert(kLoadsPerWave * kLoadWaves == kSlotBlocks, "");
 
-// Source offset of load i of this lane: LDS granule (i*8 + wave)*64 + lane of a
+// Source offset of load i of this lane: LDS granule (i*4 + wave)*64 + lane of a
 // slot is row tok = g / 72, physical granule g % 72, which holds logical granule
 // (g % 72) ^ swz(tok).  Rows at or past `valid` repeat row valid-1, so bytes past
 // a request's end are never read.
 __device__ __forceinline__ int dma_off(int i, int wave, int lane, int valid) {
-  const int gi = (i * kWaves + wave) * 64 + lane;
+  const int gi = (i * kLoadWaves + wave) * 64 + lane;
   const int tok = gi / kGranPerRow;
   const int phys = gi - tok * kGranPerRow;
   const int src_tok = tok < valid ? tok : valid - 1;
@@ -132,37 +139,30 @@ __device__ __forceinline__ int dma_off(int i, int wave, int lane, int valid) {
 }
 
 // All of this wave's direct-to-LDS loads of one chunk in one asm block: load i
-// reads base + voff[i] into the 1 KiB LDS block m0 + 8192 i (block i*8 + wave).
+// reads base + voff[i] into the 1 KiB LDS block m0 + 4096 i (block i*4 + wave).
 // The wait states cover an SGPR base just written by VALU (5) and each M0
-// update (1).  Waves 0-3 issue five loads, waves 4-7 four.
-__device__ __forceinline__ void dma_chunk(const void* base, uint32_t m0, const int (&voff)[5], bool five) {
+// update (1).
+__device__ __forceinline__ void dma_chunk(const void* base, uint32_t m0, const int (&voff)[kLoadsPerWave]) {
   const uint64_t b = (uint64_t)base;
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
   const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
   const uint64_t sbase = ((uint64_t)hi << 32) | (uint64_t)lo;
   uint32_t m = __builtin_amdgcn_readfirstlane(m0);
-  if (five) {
-    asm volatile(
-        "s_nop 4\n\t"
-        "global_load_lds_dwordx4 %1, %6\n\ts_add_u32 m0, m0, 8192\n\ts_nop 0\n\t"
-        "global_load_lds_dwordx4 %2, %6\n\ts_add_u32 m0, m0, 8192\n\ts_nop 0\n\t"
-        "global_load_lds_dwordx4 %3, %6\n\ts_add_u32 m0, m0, 8192\n\ts_nop 0\n\t"
-        "global_load_lds_dwordx4 %4, %6\n\ts_add_u32 m0, m0, 8192\n\ts_nop 0\n\t"
-        "global_load_lds_dwordx4 %5, %6"
-        : "+{m0}"(m)
-        : "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "v"(voff[4]), "s"(sbase)
-        : "memory");
-  } else {
-    asm volatile(
-        "s_nop 4\n\t"
-        "global_load_lds_dwordx4 %1, %5\n\ts_add_u32 m0, m0, 8192\n\ts_nop 0\n\t"
-        "global_load_lds_dwordx4 %2, %5\n\ts_add_u32 m0, m0, 8192\n\ts_nop 0\n\t"
-        "global_load_lds_dwordx4 %3, %5\n\ts_add_u32 m0, m0, 8192\n\ts_nop 0\n\t"
-        "global_load_lds_dwordx4 %4, %5"
-        : "+{m0}"(m)
-        : "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "s"(sbase)
-        : "memory");
-  }
+  asm volatile(
+      "s_nop 4\n\t"
+      "global_load_lds_dwordx4 %1, %10\n\ts_add_u32 m0, m0, 4096\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %10\n\ts_add_u32 m0, m0, 4096\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %3, %10\n\ts_add_u32 m0, m0, 4096\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %4, %10\n\ts_add_u32 m0, m0, 4096\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %5, %10\n\ts_add_u32 m0, m0, 4096\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %6, %10\n\ts_add_u32 m0, m0, 4096\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %7, %10\n\ts_add_u32 m0, m0, 4096\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %8, %10\n\ts_add_u32 m0, m0, 4096\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %9, %10"
+      : "+{m0}"(m)
+      : "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "v"(voff[4]), "v"(voff[5]), "v"(voff[6]),
+        "v"(voff[7]), "v"(voff[8]), "s"(sbase)
+      : "memory");
 }
 
 // The lane index, hidden from the optimiser.  Per-lane address terms derived
@@ -225,10 +225,10 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
   const int row = rb * kRowsPerBlock + row_local;
   const bool row_ok = row < a.rows;
   const int qi = row_ok ? row / a.num_heads : 0;   // which new token this row belongs to
-  const int ndma = dma_per_slot(wave);
-  int voff_full[5];   // this lane's load offsets for a full chunk
+  const bool loader = wave < kLoadWaves;
+  int voff_full[kLoadsPerWave];   // this lane's load offsets for a full chunk
 #pragma unroll
-  for (int i = 0; i < 5; i++) voff_full[i] = dma_off(i, wave, lane, kChunk);
+  for (int i = 0; i < kLoadsPerWave; i++) voff_full[i] = dma_off(i, wave & (kLoadWaves - 1), lane, kChunk);
 
   // Per-lane LDS byte offsets within a slot.
   // QK A-operand: token 16tt + n, logical granule 4k + q -> physical 8(k>>1) + ((4(k&1)) ^ y).
@@ -278,6 +278,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
     int win_pages = load_window(0);
 
     auto issue = [&](int c) {
+      if (!loader) return;
       const int t0 = t_lo + c * kChunk;
       int pw = (c >> 1) - win;   // t_lo is page aligned: two chunks per page
       if (pw >= 64) {
@@ -293,13 +294,13 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
       const int valid = t_hi - t0 < kChunk ? t_hi - t0 : kChunk;
       const uint32_t m0 = smem_addr + (c % kSlots) * kSlotBytes + wave * 1024;
       if (valid == kChunk) {
-        dma_chunk(src, m0, voff_full, ndma == 5);
+        dma_chunk(src, m0, voff_full);
       } else {   // a request's last, partial chunk
         const int l = opaque_lane();
-        int voff[5];
+        int voff[kLoadsPerWave];
 #pragma unroll
-        for (int i = 0; i < 5; i++) voff[i] = dma_off(i, wave, l, valid);
-        dma_chunk(src, m0, voff, ndma == 5);
+        for (int i = 0; i < kLoadsPerWave; i++) voff[i] = dma_off(i, wave, l, valid);
+        dma_chunk(src, m0, voff);
       }
     };
     issue(0);
@@ -330,15 +331,9 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
     for (int c = 0; c < nchunks; c++) {
       // Wait until this wave's loads of chunk c have landed (later chunks may stay in flight).
       const int ahead = (nchunks - 1 < c + kSlots - 2 ? nchunks - 1 : c + kSlots - 2) - c;
-      if (ndma == 5) {
-        if (ahead >= 2) __builtin_amdgcn_s_waitcnt(VMCNT(10));
-        else if (ahead == 1) __builtin_amdgcn_s_waitcnt(VMCNT(5));
-        else __builtin_amdgcn_s_waitcnt(VMCNT(0));
-      } else {
-        if (ahead >= 2) __builtin_amdgcn_s_waitcnt(VMCNT(8));
-        else if (ahead == 1) __builtin_amdgcn_s_waitcnt(VMCNT(4));
-        else __builtin_amdgcn_s_waitcnt(VMCNT(0));
-      }
+      if (ahead >= 2) __builtin_amdgcn_s_waitcnt(VMCNT(18));
+      else if (ahead == 1) __builtin_amdgcn_s_waitcnt(VMCNT(9));
+      else __builtin_amdgcn_s_waitcnt(VMCNT(0));
       __syncthreads();   // every wave's part of chunk c is in LDS; slot (c-1)%4 is free
       if (c + kSlots - 1 < nchunks) issue(c + kSlots - 1);
 
