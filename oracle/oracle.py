@@ -10,11 +10,13 @@ Two independent implementations live here:
   loops in double precision (see that file's header for the passages each step
   follows).
 * ``expand_attention`` is the *expand* path in NumPy float64: per-head keys and
-  values are rebuilt from the latent with W_UK and W_UV and an ordinary
-  multi-head attention with 192-wide queries/keys and 128-wide values is run
-  ("MLA inference: two computation paths and FlashMLA", section "Two
-  equivalent paths", path one).  The handbook shows both paths give the same
-  output; tests use that equivalence to pin the absorb oracle.
+  values are rebuilt from the latent with W_UK and W_UV (``expand_kv``) and an
+  ordinary multi-head attention with 192-wide queries/keys and 128-wide values
+  is run (``mha_attend``) ("MLA inference: two computation paths and
+  FlashMLA", section "Two equivalent paths", path one).  The handbook shows
+  both paths give the same output; tests use that equivalence to pin the
+  absorb oracle, and with it these two functions.
+* ``absorb_q`` / ``project_out`` are the two projections of the absorb path.
 """
 from __future__ import annotations
 
@@ -183,23 +185,49 @@ def project_out(o_latent, w_uv):
     return np.einsum("thc,hvc->thv", np.asarray(o_latent, np.float64), np.asarray(w_uv, np.float64))
 
 
+def expand_kv(latent, k_rope, w_uk, w_uv):
+    """Expand path, first step, in float64: per-head keys and values rebuilt from the cache.
+
+    latent [T, d_latent], k_rope [T, dr], w_uk and w_uv [H, dn|dv, d_latent] (k^N = W_UK[h] c).
+    Returns k [H, T, dn + dr] (k^N[h,t] then the shared k^R[t]) and v [H, T, dv].
+    ("MLA inference: two computation paths and FlashMLA", section "Two equivalent paths", path one.)
+    """
+    latent = np.asarray(latent, dtype=np.float64)
+    k_rope = np.asarray(k_rope, dtype=np.float64)
+    k_nope = np.einsum("hnc,tc->htn", np.asarray(w_uk, np.float64), latent)
+    v = np.einsum("hvc,tc->htv", np.asarray(w_uv, np.float64), latent)
+    H, T = k_nope.shape[0], k_nope.shape[1]
+    k = np.concatenate([k_nope, np.broadcast_to(k_rope[None], (H, T, k_rope.shape[1]))], axis=-1)
+    return k, v
+
+
+def mha_attend(q, k, v, softmax_scale, query_pos, key_pos):
+    """Ordinary multi-head attention in float64 with a causal rule on absolute positions.
+
+    q [Tq, H, dqk], k [H, Tk, dqk], v [H, Tk, dv]; query at position p sees keys at positions <= p.
+    Returns (out [Tq, H, dv], lse [Tq, H]); a query that sees no key gets out 0 and lse -inf.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    logits = np.einsum("qhd,htd->hqt", q, np.asarray(k, np.float64)) * softmax_scale
+    visible = np.asarray(key_pos)[None, :] <= np.asarray(query_pos)[:, None]   # [Tq, Tk]
+    logits = np.where(visible[None], logits, -np.inf)
+    mx = logits.max(axis=-1, keepdims=True)
+    safe = np.where(np.isfinite(mx), mx, 0.0)
+    w = np.exp(logits - safe)
+    z = w.sum(axis=-1, keepdims=True)
+    out = np.einsum("hqt,htv->qhv", np.divide(w, z, out=np.zeros_like(w), where=z > 0), np.asarray(v, np.float64))
+    lse = np.where(z > 0, safe + np.log(np.where(z > 0, z, 1.0)), -np.inf)[..., 0].T   # [Tq, H]
+    return out, lse
+
+
 def expand_attention(q_nope, q_rope, w_uk, w_uv, latent, k_rope, softmax_scale, query_pos, key_pos):
-    """Expand path (path one) in float64, for one request.
+    """Expand path (path one) in float64, for one request: expand_kv, then mha_attend with q = [q^N ; q^R].
 
     q_nope [Tq, H, dn], q_rope [Tq, H, dr]; w_uk, w_uv [H, dn|dv, d_latent] (k^N = W_UK[h] c);
     latent [Tk, d_latent], k_rope [Tk, dr]; query_pos [Tq] and key_pos [Tk] are absolute
     positions: query at position p sees keys at positions <= p.
     Returns (out [Tq, H, dv], lse [Tq, H]).
     """
-    latent = np.asarray(latent, dtype=np.float64)
-    k_nope = np.einsum("hnc,tc->htn", w_uk, latent)          # per-head keys rebuilt from the latent
-    v = np.einsum("hvc,tc->htv", w_uv, latent)               # per-head values rebuilt from the latent
-    logits = (np.einsum("qhn,htn->hqt", q_nope, k_nope) + np.einsum("qhr,tr->hqt", q_rope, k_rope)) * softmax_scale
-    visible = np.asarray(key_pos)[None, :] <= np.asarray(query_pos)[:, None]   # [Tq, Tk]
-    logits = np.where(visible[None], logits, -np.inf)
-    mx = logits.max(axis=-1, keepdims=True)
-    w = np.exp(logits - mx)
-    z = w.sum(axis=-1, keepdims=True)
-    out = np.einsum("hqt,htv->qhv", w / z, v)
-    lse = (mx + np.log(z))[..., 0].T                          # [Tq, H]
-    return out, lse
+    k, v = expand_kv(latent, k_rope, w_uk, w_uv)
+    q = np.concatenate([np.asarray(q_nope, np.float64), np.asarray(q_rope, np.float64)], axis=-1)
+    return mha_attend(q, k, v, softmax_scale, query_pos, key_pos)

@@ -274,3 +274,52 @@ def test_bad_block_table_and_seqlen_are_rejected():
         O.attend(wl.q, wl.cache, bt, wl.seqlens, softmax_scale=wl.softmax_scale)
     with pytest.raises(ValueError, match="seqlen"):
         O.attend(wl.q, wl.cache, wl.block_table, np.array([65], np.int32), softmax_scale=wl.softmax_scale)
+
+
+# ------------------------------------------------------------------ expand path pieces used by the prefill
+def test_mha_chunks_merged_by_lse_equal_whole():
+    """Chunked-prefix attention (the handbook's MHA_CHUNKED_KV reading): attend chunk by chunk and merge
+    with the C oracle's LSE merge -- an independent implementation -- gives the unchunked result, also for
+    chunks a causal row sees none of (lse -inf, weight 0)."""
+    rng = np.random.default_rng(21)
+    H, n, L, d = 4, 7, 150, 24
+    q = rng.standard_normal((n, H, d))
+    k = rng.standard_normal((H, L, d))
+    v = rng.standard_normal((H, L, 10))
+    qpos, kpos = np.arange(L - n, L), np.arange(L)
+    whole_o, whole_l = O.mha_attend(q, k, v, 0.3, qpos, kpos)
+    cuts = [0, 40, 41, 97, 146, 148, L]   # the last chunks are partly or wholly after some queries
+    outs, lses = [], []
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        o, l = O.mha_attend(q, k[:, a:b], v[:, a:b], 0.3, qpos, kpos[a:b])
+        outs.append(o.reshape(n * H, -1))
+        lses.append(l.reshape(n * H))
+    assert np.isneginf(lses[-1]).sum() == 5 * H     # queries at positions 143-147 see none of [148, 150)
+    mo, ml = O.lse_merge(np.stack(outs), np.stack(lses))
+    np.testing.assert_allclose(mo, whole_o.reshape(n * H, -1), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(ml, whole_l.reshape(n * H), rtol=0, atol=1e-12)
+
+
+def test_mha_one_key_copies_the_value():
+    """With one visible key p = 1, so out = v and lse = scale * (q . k) (closed form)."""
+    rng = np.random.default_rng(22)
+    q, k, v = rng.standard_normal((1, 3, 8)), rng.standard_normal((3, 1, 8)), rng.standard_normal((3, 1, 5))
+    o, l = O.mha_attend(q, k, v, 0.5, np.array([4]), np.array([4]))
+    np.testing.assert_array_equal(o[0], v[:, 0])
+    np.testing.assert_allclose(l[0], 0.5 * np.einsum("hd,hd->h", q[0], k[:, 0]), rtol=0, atol=1e-14)
+    o, l = O.mha_attend(q, k, v, 0.5, np.array([3]), np.array([4]))   # the key is in the future
+    assert (o == 0).all() and np.isneginf(l).all()
+
+
+def test_expand_kv_shapes_and_shared_rope():
+    """k = [W_UK[h] c ; k^R] with k^R shared by every head, v = W_UV[h] c (path one of the handbook)."""
+    rng = np.random.default_rng(23)
+    c, kr = rng.standard_normal((5, 16)), rng.standard_normal((5, 4))
+    wuk, wuv = rng.standard_normal((3, 6, 16)), rng.standard_normal((3, 7, 16))
+    k, v = O.expand_kv(c, kr, wuk, wuv)
+    assert k.shape == (3, 5, 10) and v.shape == (3, 5, 7)
+    for h in range(3):
+        for t in range(5):
+            np.testing.assert_allclose(k[h, t, :6], wuk[h] @ c[t], rtol=0, atol=1e-12)
+            np.testing.assert_array_equal(k[h, t, 6:], kr[t])
+            np.testing.assert_allclose(v[h, t], wuv[h] @ c[t], rtol=0, atol=1e-12)
