@@ -35,7 +35,8 @@ PAGE_SIZE = 64
 SOFTMAX_SCALE = 1.0 / math.sqrt(128 + 64)
 
 EXPORTED_SYMBOLS = ("mla_get_workspace", "mla_decode_fwd", "mla_splitkv_combine", "mla_workspace_flags",
-                    "mla_status_string", "mla_absorb_q", "mla_project_out")
+                    "mla_status_string", "mla_absorb_q", "mla_project_out", "mla_expand_kv",
+                    "mla_prefill_attention", "mla_lse_merge", "mla_prefill_workspace_size", "mla_chunked_prefill")
 D_NOPE, D_ROPE, D_LATENT, D_V = 128, 64, 512, 128
 
 
@@ -61,6 +62,21 @@ class ProjParams(ctypes.Structure):
 
 def make_proj_params(*, tokens, num_heads, d_nope=D_NOPE, d_rope=D_ROPE, d_latent=D_LATENT, d_v=D_V) -> ProjParams:
     return ProjParams(tokens, num_heads, d_nope, d_rope, d_latent, d_v)
+
+
+class PrefillParams(ctypes.Structure):
+    """Mirror of mla_prefill_params."""
+    _fields_ = [("num_heads", ctypes.c_int32), ("num_new", ctypes.c_int32), ("seqlen", ctypes.c_int32),
+                ("num_pages", ctypes.c_int32), ("max_blocks", ctypes.c_int32), ("chunk_tokens", ctypes.c_int32),
+                ("softmax_scale", ctypes.c_float), ("d_nope", ctypes.c_int32), ("d_rope", ctypes.c_int32),
+                ("d_latent", ctypes.c_int32), ("d_v", ctypes.c_int32)]
+
+
+def make_prefill_params(*, num_heads, num_new, seqlen, num_pages, max_blocks, chunk_tokens=4096,
+                        softmax_scale=1.0 / math.sqrt(D_NOPE + D_ROPE), d_nope=D_NOPE, d_rope=D_ROPE,
+                        d_latent=D_LATENT, d_v=D_V) -> PrefillParams:
+    return PrefillParams(num_heads, num_new, seqlen, num_pages, max_blocks, chunk_tokens, softmax_scale, d_nope,
+                         d_rope, d_latent, d_v)
 
 
 def make_params(*, batch, seqlen_q, num_heads, num_pages, max_blocks_per_seq, kv_dtype=MLA_KV_BF16, causal=False,
@@ -92,8 +108,16 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     ppp = ctypes.POINTER(ProjParams)
     lib.mla_absorb_q.argtypes = [ppp, vp, vp, vp, vp, vp]
     lib.mla_project_out.argtypes = [ppp, vp, vp, vp, vp]
-    for name in ("mla_get_workspace", "mla_decode_fwd", "mla_splitkv_combine", "mla_workspace_flags", "mla_absorb_q",
-                 "mla_project_out"):
+    pfp = ctypes.POINTER(PrefillParams)
+    i32 = ctypes.c_int32
+    lib.mla_expand_kv.argtypes = [pfp, vp, vp, i32, i32, vp, vp, vp, vp, vp]
+    lib.mla_prefill_attention.argtypes = [pfp, vp, vp, vp, i32, i32, vp, vp, vp]
+    lib.mla_lse_merge.argtypes = [i32, i32, vp, vp, vp, vp, vp]
+    lib.mla_prefill_workspace_size.argtypes = [pfp, ctypes.POINTER(sz)]
+    lib.mla_chunked_prefill.argtypes = [pfp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
+    for name in EXPORTED_SYMBOLS:
+        if name == "mla_status_string":
+            continue
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -180,6 +204,78 @@ def project_out(o_latent, w_uv, out=None):
     mla_project_out(make_proj_params(tokens=T, num_heads=H), o_latent.data_ptr(), w_uv.data_ptr(), out.data_ptr(),
                     torch.cuda.current_stream(o_latent.device).cuda_stream)
     return out
+
+
+def mla_expand_kv(params: PrefillParams, kv_ptr: int, block_table_ptr: int, t0: int, ntok: int, w_uk_ptr: int,
+                  w_uv_ptr: int, k_ptr: int, vt_ptr: int, stream: int = 0) -> None:
+    _check("mla_expand_kv", load_library().mla_expand_kv(
+        ctypes.byref(params), kv_ptr or None, block_table_ptr or None, t0, ntok, w_uk_ptr or None, w_uv_ptr or None,
+        k_ptr or None, vt_ptr or None, stream or None))
+
+
+def mla_prefill_attention(params: PrefillParams, q_ptr: int, k_ptr: int, vt_ptr: int, t0: int, ntok: int,
+                          out_ptr: int, lse_ptr: int, stream: int = 0) -> None:
+    _check("mla_prefill_attention", load_library().mla_prefill_attention(
+        ctypes.byref(params), q_ptr or None, k_ptr or None, vt_ptr or None, t0, ntok, out_ptr or None,
+        lse_ptr or None, stream or None))
+
+
+def mla_lse_merge(rows: int, nparts: int, parts_ptr: int, lparts_ptr: int, out_ptr: int, lse_ptr: int,
+                  stream: int = 0) -> None:
+    _check("mla_lse_merge", load_library().mla_lse_merge(
+        rows, nparts, parts_ptr or None, lparts_ptr or None, out_ptr or None, lse_ptr or None, stream or None))
+
+
+def mla_prefill_workspace_size(params: PrefillParams) -> int:
+    n = ctypes.c_size_t(0)
+    _check("mla_prefill_workspace_size", load_library().mla_prefill_workspace_size(ctypes.byref(params),
+                                                                                   ctypes.byref(n)))
+    return n.value
+
+
+def mla_chunked_prefill(params: PrefillParams, q_ptr: int, kv_ptr: int, block_table_ptr: int, w_uk_ptr: int,
+                        w_uv_ptr: int, workspace_ptr: int, workspace_bytes: int, out_ptr: int, lse_ptr: int,
+                        stream: int = 0) -> None:
+    _check("mla_chunked_prefill", load_library().mla_chunked_prefill(
+        ctypes.byref(params), q_ptr or None, kv_ptr or None, block_table_ptr or None, w_uk_ptr or None,
+        w_uv_ptr or None, workspace_ptr or None, workspace_bytes, out_ptr or None, lse_ptr or None, stream or None))
+
+
+class MlaPrefill:
+    """The expand path for one request's new tokens on torch device tensors.
+
+    q: bf16 [n, H, 192]; kv: the bf16 paged cache [P, 64, 576]; block_table: int32 row of the
+    request; w_uk, w_uv: bf16 [H, 128, 512].  The workspace is allocated once here.
+    """
+
+    def __init__(self, *, num_heads, num_new, seqlen, num_pages, max_blocks, chunk_tokens=4096,
+                 softmax_scale=1.0 / math.sqrt(D_NOPE + D_ROPE), device="cuda"):
+        import torch
+        self.params = make_prefill_params(num_heads=num_heads, num_new=num_new, seqlen=seqlen, num_pages=num_pages,
+                                          max_blocks=max_blocks, chunk_tokens=chunk_tokens,
+                                          softmax_scale=softmax_scale)
+        self.ws_bytes = mla_prefill_workspace_size(self.params)
+        self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
+
+    def __call__(self, q, kv, block_table, w_uk, w_uv, out=None, lse=None):
+        import torch
+        p = self.params
+        n, H = p.num_new, p.num_heads
+        _bf16_tensor(q, (n, H, D_NOPE + D_ROPE), "q")
+        _bf16_tensor(w_uk, (H, D_NOPE, D_LATENT), "w_uk")
+        _bf16_tensor(w_uv, (H, D_V, D_LATENT), "w_uv")
+        if kv.element_size() != 2 or not kv.is_contiguous() or tuple(kv.shape[1:]) != (64, D_LATENT + D_ROPE):
+            raise ValueError(f"kv: expected a contiguous 16-bit [P, 64, 576] cache, got {tuple(kv.shape)}")
+        if block_table.dtype != torch.int32 or block_table.numel() < p.max_blocks or not block_table.is_contiguous():
+            raise ValueError("block_table: expected a contiguous int32 row of max_blocks entries")
+        if out is None:
+            out = torch.empty((n, H, D_V), dtype=q.dtype, device=q.device)
+        if lse is None:
+            lse = torch.empty((n, H), dtype=torch.float32, device=q.device)
+        mla_chunked_prefill(p, q.data_ptr(), kv.data_ptr(), block_table.data_ptr(), w_uk.data_ptr(), w_uv.data_ptr(),
+                            self.workspace.data_ptr(), self.ws_bytes, out.data_ptr(), lse.data_ptr(),
+                            torch.cuda.current_stream(q.device).cuda_stream)
+        return out, lse
 
 
 class MlaDecode:

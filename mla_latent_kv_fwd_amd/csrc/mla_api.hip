@@ -10,6 +10,7 @@
 #define MLA_HD __host__ __device__
 #include "mla_decode.h"
 #include "mla_proj.h"
+#include "mla_prefill.h"
 #include "mla_launch.h"
 #include "mla_workspace.h"
 
@@ -79,6 +80,45 @@ int validate_proj(const mla_proj_params* p) {
 }
 
 bool misaligned16(const void* ptr) { return ((uintptr_t)ptr & 15) != 0; }
+
+constexpr int kMaxPrefillNew = 65536;
+constexpr int kMaxChunkTokens = 65536;
+constexpr int kMaxMergeParts = 4096;
+
+int validate_prefill(const mla_prefill_params* p) {
+  if (!p) return MLA_ERR_INVALID_ARG;
+  if (p->num_heads < 1 || p->num_new < 1 || p->num_new > kMaxPrefillNew || p->seqlen < p->num_new)
+    return MLA_ERR_INVALID_ARG;
+  if (p->num_pages < 1 || p->max_blocks < 1) return MLA_ERR_INVALID_ARG;
+  if ((int64_t)p->max_blocks * kPageSize >= ((int64_t)1 << 31)) return MLA_ERR_UNSUPPORTED;
+  if ((int64_t)p->seqlen > (int64_t)p->max_blocks * kPageSize) return MLA_ERR_INVALID_ARG;
+  if (p->chunk_tokens < 64 || p->chunk_tokens > kMaxChunkTokens || p->chunk_tokens % 64) return MLA_ERR_INVALID_ARG;
+  if (!(p->softmax_scale > 0.f) || !isfinite(p->softmax_scale)) return MLA_ERR_INVALID_ARG;
+  if (p->num_heads > kMaxHeads) return MLA_ERR_UNSUPPORTED;
+  if (p->d_nope != 128 || p->d_rope != 64 || p->d_latent != 512 || p->d_v != 128) return MLA_ERR_UNSUPPORTED;
+  if ((p->seqlen + p->chunk_tokens - 1) / p->chunk_tokens > kMaxMergeParts) return MLA_ERR_UNSUPPORTED;
+  return MLA_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Chunked-prefill workspace: one expanded K and V^T chunk, then the fp32 partials and
+// LSEs of every chunk.
+struct PrefillLayout {
+  size_t k, vt, parts, lparts, total;
+  int nchunks;
+};
+PrefillLayout prefill_layout(const mla_prefill_params* p) {
+  PrefillLayout l;
+  const size_t H = p->num_heads, Tc = p->chunk_tokens, rows = (size_t)p->num_new * H;
+  l.nchunks = (p->seqlen + p->chunk_tokens - 1) / p->chunk_tokens;
+  l.k = 0;
+  l.vt = align256(l.k + H * Tc * 192 * 2);
+  l.parts = align256(l.vt + H * 128 * Tc * 2);
+  l.lparts = align256(l.parts + (size_t)l.nchunks * rows * 128 * 4);
+  l.total = align256(l.lparts + (size_t)l.nchunks * rows * 4);
+  return l;
+}
 
 }  // namespace
 
@@ -202,6 +242,92 @@ int mla_workspace_flags(const void* workspace, uint32_t* flags, void* stream) {
   Header h;
   if (hipMemcpy(&h, workspace, sizeof h, hipMemcpyDeviceToHost) != hipSuccess) return MLA_ERR_HIP;
   *flags = h.magic == kMagic ? h.flags : 0u;
+  return MLA_OK;
+}
+
+int mla_expand_kv(const mla_prefill_params* p, const void* kv_cache, const int32_t* block_table, int32_t t0,
+                  int32_t ntok, const void* w_uk, const void* w_uv, void* k_out, void* vt_out, void* stream) {
+  const int st = validate_prefill(p);
+  if (st != MLA_OK) return st;
+  if (!kv_cache || !block_table || !w_uk || !w_uv || !k_out || !vt_out) return MLA_ERR_INVALID_ARG;
+  if (misaligned16(kv_cache) || misaligned16(w_uk) || misaligned16(w_uv) || misaligned16(k_out) || misaligned16(vt_out))
+    return MLA_ERR_INVALID_ARG;
+  if (t0 < 0 || ntok < 1 || ntok > kMaxChunkTokens || (int64_t)t0 + ntok > p->seqlen) return MLA_ERR_INVALID_ARG;
+  if (launch_expand_kv(static_cast<const uint16_t*>(kv_cache), block_table, t0, ntok, p->num_pages,
+                       static_cast<const uint16_t*>(w_uk), static_cast<const uint16_t*>(w_uv),
+                       static_cast<uint16_t*>(k_out), static_cast<uint16_t*>(vt_out), p->num_heads,
+                       (hipStream_t)stream) != hipSuccess)
+    return MLA_ERR_HIP;
+  return MLA_OK;
+}
+
+int mla_prefill_attention(const mla_prefill_params* p, const void* q, const void* k, const void* vt, int32_t t0,
+                          int32_t ntok, float* out, float* lse, void* stream) {
+  const int st = validate_prefill(p);
+  if (st != MLA_OK) return st;
+  if (!q || !k || !vt || !out || !lse) return MLA_ERR_INVALID_ARG;
+  if (misaligned16(q) || misaligned16(k) || misaligned16(vt) || misaligned16(out) || ((uintptr_t)lse & 3))
+    return MLA_ERR_INVALID_ARG;
+  if (t0 < 0 || ntok < 1 || ntok > kMaxChunkTokens || (int64_t)t0 + ntok > p->seqlen) return MLA_ERR_INVALID_ARG;
+  if (launch_prefill_attention(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                               static_cast<const uint16_t*>(vt), t0, ntok, p->num_new, p->seqlen, p->num_heads,
+                               p->softmax_scale, out, lse, (hipStream_t)stream) != hipSuccess)
+    return MLA_ERR_HIP;
+  return MLA_OK;
+}
+
+int mla_lse_merge(int32_t rows, int32_t nparts, const float* out_parts, const float* lse_parts, void* out, float* lse,
+                  void* stream) {
+  if (rows < 1 || rows > (1 << 24) || nparts < 1 || nparts > kMaxMergeParts) return MLA_ERR_INVALID_ARG;
+  if (!out_parts || !lse_parts || !out || !lse) return MLA_ERR_INVALID_ARG;
+  if (misaligned16(out_parts) || misaligned16(out) || ((uintptr_t)lse_parts & 3) || ((uintptr_t)lse & 3))
+    return MLA_ERR_INVALID_ARG;
+  if (launch_lse_merge(rows, nparts, out_parts, lse_parts, static_cast<uint16_t*>(out), lse, (hipStream_t)stream) !=
+      hipSuccess)
+    return MLA_ERR_HIP;
+  return MLA_OK;
+}
+
+int mla_prefill_workspace_size(const mla_prefill_params* p, size_t* bytes) {
+  const int st = validate_prefill(p);
+  if (st != MLA_OK) return st;
+  if (!bytes) return MLA_ERR_INVALID_ARG;
+  *bytes = prefill_layout(p).total;
+  return MLA_OK;
+}
+
+int mla_chunked_prefill(const mla_prefill_params* p, const void* q, const void* kv_cache, const int32_t* block_table,
+                        const void* w_uk, const void* w_uv, void* workspace, size_t workspace_bytes, void* out,
+                        float* lse, void* stream) {
+  const int st = validate_prefill(p);
+  if (st != MLA_OK) return st;
+  if (!q || !kv_cache || !block_table || !w_uk || !w_uv || !workspace || !out || !lse) return MLA_ERR_INVALID_ARG;
+  if (misaligned16(q) || misaligned16(kv_cache) || misaligned16(w_uk) || misaligned16(w_uv) || misaligned16(out) ||
+      ((uintptr_t)workspace & 255) || ((uintptr_t)lse & 3))
+    return MLA_ERR_INVALID_ARG;
+  const PrefillLayout l = prefill_layout(p);
+  if (workspace_bytes < l.total) return MLA_ERR_WORKSPACE_TOO_SMALL;
+  char* ws = static_cast<char*>(workspace);
+  uint16_t* kbuf = reinterpret_cast<uint16_t*>(ws + l.k);
+  uint16_t* vtbuf = reinterpret_cast<uint16_t*>(ws + l.vt);
+  float* parts = reinterpret_cast<float*>(ws + l.parts);
+  float* lparts = reinterpret_cast<float*>(ws + l.lparts);
+  const size_t rows = (size_t)p->num_new * p->num_heads;
+  const hipStream_t s = (hipStream_t)stream;
+  for (int j = 0; j < l.nchunks; j++) {
+    const int t0 = j * p->chunk_tokens;
+    const int ntok = p->seqlen - t0 < p->chunk_tokens ? p->seqlen - t0 : p->chunk_tokens;
+    if (launch_expand_kv(static_cast<const uint16_t*>(kv_cache), block_table, t0, ntok, p->num_pages,
+                         static_cast<const uint16_t*>(w_uk), static_cast<const uint16_t*>(w_uv), kbuf, vtbuf,
+                         p->num_heads, s) != hipSuccess)
+      return MLA_ERR_HIP;
+    if (launch_prefill_attention(static_cast<const uint16_t*>(q), kbuf, vtbuf, t0, ntok, p->num_new, p->seqlen,
+                                 p->num_heads, p->softmax_scale, parts + (size_t)j * rows * 128,
+                                 lparts + (size_t)j * rows, s) != hipSuccess)
+      return MLA_ERR_HIP;
+  }
+  if (launch_lse_merge((int)rows, l.nchunks, parts, lparts, static_cast<uint16_t*>(out), lse, s) != hipSuccess)
+    return MLA_ERR_HIP;
   return MLA_OK;
 }
 

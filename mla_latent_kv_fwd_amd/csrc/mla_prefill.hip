@@ -1,0 +1,463 @@
+// mla_prefill.hip -- the expand path for one request's new tokens (declared in
+// include/mla_prefill.h): expansion of cached latents into per-head keys and
+// values, multi-head attention over one expanded chunk, and the LSE merge of
+// the chunks.  ("MLA inference: two computation paths and FlashMLA", section
+// "Two equivalent paths", path one; the same page's engine notes expand a long
+// prefix in chunks and merge the chunks by LSE.)
+//
+// All contractions run on v_mfma_f32_16x16x32_bf16 with fp32 accumulation.
+//
+// Expansion is a GEMM [tokens x 512] x [512 x (H x 256)] with the latent rows
+// gathered through the block table.  A workgroup owns 128 tokens and one head
+// and stages 64 latent columns at a time of the latent tile and both weight
+// tiles in LDS (double-buffered); waves 0-3 form k^N as C[n][t] (lane holds four
+// consecutive n of one token: 8-byte stores into k[h][t][:]), waves 4-7 form v
+// as C[t][v] (four consecutive tokens of one dim: 8-byte stores into v^T).
+//
+// Attention keeps the decode kernel's orientation -- scores as S^T = K . q^T,
+// lane = query -- with 32 queries per wave, so every K or V^T fragment read
+// from LDS feeds two MFMAs.  The rows of the two 16-token score tiles of a
+// 32-token group are permuted (tile a: tokens 8(m/4) + m%4, tile b: + 4) so
+// that a lane's eight probabilities are tokens 8g .. 8g+7 of the group: the
+// B-operand of O^T += V^T . P^T with V^T read straight from a dims-major LDS
+// tile.  Online softmax with the lazy rescale of the decode kernel.
+#include <hip/hip_runtime.h>
+
+#define MLA_HD __host__ __device__
+#include "mla_launch.h"
+
+namespace mla {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr int kNope = 128, kRope = 64, kLat = 512, kDv = 128;
+constexpr int kQK = kNope + kRope;   // 192
+constexpr int kCacheRow = kLat + kRope;   // 576 numbers per cached token
+constexpr int kPage = 64;
+constexpr float kLazyRescale = 8.0f;      // log2 of the largest p kept unrescaled
+constexpr float kLn2 = 0.69314718055994531f;
+
+__device__ __forceinline__ bf16x8_t lds_b128(const char LDS_AS* p) { return *reinterpret_cast<const bf16x8_t LDS_AS*>(p); }
+__device__ __forceinline__ void lds_w128(char LDS_AS* p, bf16x8_t v) { *reinterpret_cast<bf16x8_t LDS_AS*>(p) = v; }
+
+__device__ __forceinline__ float row_max(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float row_sum(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// ===========================================================================
+// Expansion
+// ===========================================================================
+constexpr int kExpTok = 128;               // tokens per workgroup
+constexpr int kExpC = 64;                  // latent columns per stage
+constexpr int kExpStages = kLat / kExpC;   // 8
+constexpr int kExpThreads = 512;
+constexpr int kExpTile = 128 * kExpC * 2;  // 16 KiB: 128 rows x 64 columns, 128-byte rows
+// Row r of a tile: granule j (8 columns) stored at granule j ^ ((r >> 1) & 7), so
+// 16 lanes reading one granule of 16 consecutive rows hit 16 bank groups.
+__device__ __forceinline__ int exp_off(int r, int j) { return r * 128 + ((j ^ ((r >> 1) & 7)) << 4); }
+
+__global__ __launch_bounds__(kExpThreads) void mla_expand_kv_kernel(const uint16_t* __restrict__ cache,
+                                                                   const int32_t* __restrict__ block_table, int t0,
+                                                                   int ntok, int ld, int num_pages,
+                                                                   const uint16_t* __restrict__ w_uk,
+                                                                   const uint16_t* __restrict__ w_uv,
+                                                                   uint16_t* __restrict__ k_out,
+                                                                   uint16_t* __restrict__ vt_out, int H) {
+  // [buffer][lat | W_UK | W_UV]
+  __shared__ __attribute__((aligned(16))) char smem[2 * 3 * kExpTile];
+  char LDS_AS* lds = (char LDS_AS*)smem;
+  const int tile_t = blockIdx.x * kExpTok;   // first token (of the range) of this tile
+  const int h = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, r = lane & 15;
+
+  // Cached row of token j of the tile (nullptr past the range: zeros).
+  auto token_row = [&](int j) -> const uint16_t* {
+    const int t = tile_t + j;
+    if (t >= ntok) return nullptr;
+    const int pos = t0 + t;
+    int page = block_table[pos / kPage];
+    page = (page < 0 || page >= num_pages) ? 0 : page;
+    return cache + ((size_t)page * kPage + pos % kPage) * kCacheRow;
+  };
+
+  // k^R: k[h][t][128 .. 191] = cached RoPE key of token t (zeros past the range).
+  for (int i = tid; i < kExpTok * (kRope / 8); i += kExpThreads) {
+    const int j = i >> 3, part = i & 7;
+    if (tile_t + j >= ld) continue;
+    const uint16_t* row = token_row(j);
+    const bf16x8_t v = row ? *reinterpret_cast<const bf16x8_t*>(row + kLat + 8 * part) : bf16x8_t{};
+    *reinterpret_cast<bf16x8_t*>(k_out + ((size_t)h * ld + tile_t + j) * kQK + kNope + 8 * part) = v;
+  }
+
+  // Stage loads: 3 tiles x 1,024 granules over 512 threads, two granules of each per thread.
+  const uint16_t* lat_row[2];
+  int lr[2], lj[2];
+#pragma unroll
+  for (int u = 0; u < 2; u++) {
+    const int gi = tid + u * kExpThreads;   // 0 .. 1023
+    lr[u] = gi >> 3;
+    lj[u] = gi & 7;
+    lat_row[u] = token_row(lr[u]);
+  }
+  const uint16_t* wk = w_uk + (size_t)h * kNope * kLat;
+  const uint16_t* wv = w_uv + (size_t)h * kDv * kLat;
+  bf16x8_t pre[6];
+  auto fetch = [&](int st) {
+    const int c0 = st * kExpC;
+#pragma unroll
+    for (int u = 0; u < 2; u++) {
+      pre[u] = lat_row[u] ? *reinterpret_cast<const bf16x8_t*>(lat_row[u] + c0 + 8 * lj[u]) : bf16x8_t{};
+      pre[2 + u] = *reinterpret_cast<const bf16x8_t*>(wk + (size_t)lr[u] * kLat + c0 + 8 * lj[u]);
+      pre[4 + u] = *reinterpret_cast<const bf16x8_t*>(wv + (size_t)lr[u] * kLat + c0 + 8 * lj[u]);
+    }
+  };
+  auto stash = [&](int buf) {
+    char LDS_AS* base = lds + buf * 3 * kExpTile;
+#pragma unroll
+    for (int u = 0; u < 2; u++) {
+      const int off = exp_off(lr[u], lj[u]);
+      lds_w128(base + off, pre[u]);
+      lds_w128(base + kExpTile + off, pre[2 + u]);
+      lds_w128(base + 2 * kExpTile + off, pre[4 + u]);
+    }
+  };
+
+  // Waves 0-3: k^N tile C[n][t] (A = W_UK rows, B = latent rows); waves 4-7: C[t][v]
+  // (A = latent rows, B = W_UV rows).  Each wave owns 64 x 64 of the 128 x 128 tile:
+  // rows 64 (w & 1) + 16 i, columns 64 ((w >> 1) & 1) + 16 j.
+  const bool is_k = wave < 4;
+  const int wq = wave & 3;
+  const int row0 = 64 * (wq & 1), col0 = 64 * (wq >> 1);
+  const int a_tile = is_k ? 1 : 0;   // tile index of the A operand (W_UK or latent)
+  const int b_tile = is_k ? 0 : 2;   // tile index of the B operand (latent or W_UV)
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+#pragma unroll
+    for (int j = 0; j < 4; j++) acc[i][j] = f32x4_t{};
+
+  fetch(0);
+  stash(0);
+  __syncthreads();
+  for (int st = 0; st < kExpStages; st++) {
+    if (st + 1 < kExpStages) fetch(st + 1);
+    const char LDS_AS* base = lds + (st & 1) * 3 * kExpTile;
+#pragma unroll
+    for (int ks = 0; ks < kExpC / 32; ks++) {
+      bf16x8_t af[4], bfr[4];
+#pragma unroll
+      for (int i = 0; i < 4; i++) af[i] = lds_b128(base + a_tile * kExpTile + exp_off(row0 + 16 * i + r, 4 * ks + g));
+#pragma unroll
+      for (int j = 0; j < 4; j++) bfr[j] = lds_b128(base + b_tile * kExpTile + exp_off(col0 + 16 * j + r, 4 * ks + g));
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+    if (st + 1 < kExpStages) {
+      stash((st + 1) & 1);   // buffer (st+1)&1 was last read in stage st-1, before the barrier below it
+    }
+    __syncthreads();
+  }
+
+  // Lane (g, r) holds C[row0 + 16 i + 4 g + e][col0 + 16 j + r], e = 0..3.
+  if (is_k) {
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const int t = tile_t + col0 + 16 * j + r;
+      if (t >= ld) continue;
+      uint16_t* dst = k_out + ((size_t)h * ld + t) * kQK;
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        bf16x4_t w;
+#pragma unroll
+        for (int e = 0; e < 4; e++) w[e] = (__bf16)acc[i][j][e];
+        *reinterpret_cast<bf16x4_t*>(dst + row0 + 16 * i + 4 * g) = w;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int t = tile_t + row0 + 16 * i + 4 * g;   // ld is a multiple of 64: t < ld covers t + 3
+      if (t >= ld) continue;
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const int v = col0 + 16 * j + r;
+        bf16x4_t w;
+#pragma unroll
+        for (int e = 0; e < 4; e++) w[e] = (__bf16)acc[i][j][e];
+        *reinterpret_cast<bf16x4_t*>(vt_out + ((size_t)h * kDv + v) * ld + t) = w;
+      }
+    }
+  }
+}
+
+// ===========================================================================
+// Attention over one expanded chunk
+// ===========================================================================
+constexpr int kAttThreads = 256;
+constexpr int kAttQ = 128;                   // queries per workgroup (4 waves x 32)
+constexpr int kKBlk = 64;                    // keys per LDS block
+constexpr int kKBytes = kKBlk * kQK * 2;     // 24 KiB: 64 rows x 384 bytes
+constexpr int kVBytes = kDv * kKBlk * 2;     // 16 KiB: 128 dim rows x 128 bytes
+constexpr int kStage = kKBytes + kVBytes;    // 40 KiB
+constexpr int kGranK = kKBlk * (kQK / 8);    // 1,536 granules
+constexpr int kGranV = kDv * (kKBlk / 8);    // 1,024 granules
+static_assert(kGranK % kAttThreads == 0 && kGranV % kAttThreads == 0, "whole granules per thread");
+
+// K rows (384 bytes, 24 granules): the low 3 bits of the granule index are XORed
+// with bits (1, 3, 4) of the token, which makes the 16 (permuted) token rows of a
+// score tile land in 16 bank groups.  V^T rows (128 bytes): granule ^ ((d >> 1) & 7).
+__device__ __forceinline__ int k_off(int t, int j) {
+  const int s = ((t >> 1) & 1) | ((t >> 2) & 6);
+  return t * (kQK * 2) + (((j & ~7) | ((j & 7) ^ s)) << 4);
+}
+__device__ __forceinline__ int v_off(int d, int j) { return kKBytes + d * (kKBlk * 2) + ((j ^ ((d >> 1) & 7)) << 4); }
+
+__global__ __launch_bounds__(kAttThreads, 2) void mla_prefill_attention_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kbuf, const uint16_t* __restrict__ vtbuf, int t0,
+    int ntok, int ld, int n, int L, int H, float scale_log2, float* __restrict__ out, float* __restrict__ lse) {
+  __shared__ __attribute__((aligned(16))) char smem[2 * kStage];
+  char LDS_AS* lds = (char LDS_AS*)smem;
+  const int h = blockIdx.y;
+  const int qb = blockIdx.x * kAttQ;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, r = lane & 15;
+
+  // Key blocks this workgroup needs: positions up to its last query's.
+  const int qlast = min(qb + kAttQ - 1, n - 1);
+  const int pos_first = L - n + qb;       // position of the first query of the block
+  const int pos_last = L - n + qlast;
+  const int nblk_all = ld / kKBlk;
+  const int nblk = pos_last < t0 ? 0 : min(nblk_all, (pos_last - t0) / kKBlk + 1);
+
+  // This wave's queries: tiles qt = 0, 1 of 16; lane r is query qw + 16 qt + r.
+  const int qw = qb + 32 * wave;
+  bf16x8_t qf[2][kQK / 32];
+  int qpos[2];
+#pragma unroll
+  for (int qt = 0; qt < 2; qt++) {
+    const int qi = qw + 16 * qt + r;
+    const bool ok = qi < n;
+    qpos[qt] = L - n + qi;
+    const uint16_t* qrow = q + ((size_t)(ok ? qi : 0) * H + h) * kQK + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < kQK / 32; ks++) {
+      const bf16x8_t v = *reinterpret_cast<const bf16x8_t*>(qrow + 32 * ks);
+      qf[qt][ks] = ok ? v : bf16x8_t{};
+    }
+  }
+
+  // Block loads: K granules gi = tid + 256 u (u < 6), V^T granules x = tid + 256 u (u < 4).
+  const uint16_t* kh = kbuf + (size_t)h * ld * kQK;
+  const uint16_t* vh = vtbuf + (size_t)h * kDv * ld;
+  constexpr int kUK = kGranK / kAttThreads, kUV = kGranV / kAttThreads;   // 6, 4
+  bf16x8_t pre[kUK + kUV];
+  auto fetch = [&](int kb) {
+#pragma unroll
+    for (int u = 0; u < kUK; u++) {
+      const int gi = tid + u * kAttThreads;
+      const int t = gi / (kQK / 8), j = gi % (kQK / 8);
+      pre[u] = *reinterpret_cast<const bf16x8_t*>(kh + (size_t)(kb * kKBlk + t) * kQK + 8 * j);
+    }
+#pragma unroll
+    for (int u = 0; u < kUV; u++) {
+      const int x = tid + u * kAttThreads, d = x >> 3, j = x & 7;
+      pre[kUK + u] = *reinterpret_cast<const bf16x8_t*>(vh + (size_t)d * ld + kb * kKBlk + 8 * j);
+    }
+  };
+  auto stash = [&](int buf) {
+    char LDS_AS* base = lds + buf * kStage;
+#pragma unroll
+    for (int u = 0; u < kUK; u++) {
+      const int gi = tid + u * kAttThreads;
+      lds_w128(base + k_off(gi / (kQK / 8), gi % (kQK / 8)), pre[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kUV; u++) {
+      const int x = tid + u * kAttThreads;
+      lds_w128(base + v_off(x >> 3, x & 7), pre[kUK + u]);
+    }
+  };
+
+  float m_ref[2] = {-INFINITY, -INFINITY};   // reference maximum (log2 units) per query tile
+  float lsum[2] = {0.f, 0.f};
+  f32x4_t o[2][kDv / 16];
+#pragma unroll
+  for (int qt = 0; qt < 2; qt++)
+#pragma unroll
+    for (int dt = 0; dt < kDv / 16; dt++) o[qt][dt] = f32x4_t{};
+
+  // Score-tile row m of tile a is token 8(m/4) + m%4 of the 32-token group; tile b adds 4.
+  const int ta = 8 * (r >> 2) + (r & 3);
+
+  if (nblk > 0) {
+    fetch(0);
+    stash(0);
+  }
+  __syncthreads();
+  for (int kb = 0; kb < nblk; kb++) {
+    if (kb + 1 < nblk) fetch(kb + 1);
+    const char LDS_AS* base = lds + (kb & 1) * kStage;
+    const int kpos0 = t0 + kb * kKBlk;   // position of the block's first key
+    const bool need_mask = (kb * kKBlk + kKBlk > ntok) || (kpos0 + kKBlk - 1 > pos_first);
+#pragma unroll
+    for (int grp = 0; grp < 2; grp++) {
+      f32x4_t s[2][2];   // [query tile][score tile a/b]
+#pragma unroll
+      for (int qt = 0; qt < 2; qt++) s[qt][0] = s[qt][1] = f32x4_t{};
+#pragma unroll
+      for (int ks = 0; ks < kQK / 32; ks++) {
+        const bf16x8_t ka = lds_b128(base + k_off(32 * grp + ta, 4 * ks + g));
+        const bf16x8_t kbf = lds_b128(base + k_off(32 * grp + ta + 4, 4 * ks + g));
+#pragma unroll
+        for (int qt = 0; qt < 2; qt++) {
+          s[qt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[qt][ks], s[qt][0], 0, 0, 0);
+          s[qt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kbf, qf[qt][ks], s[qt][1], 0, 0, 0);
+        }
+      }
+      // s[qt][0][e] is token 32 grp + 8g + e, s[qt][1][e] token 32 grp + 8g + 4 + e.
+      bf16x8_t pb[2];
+#pragma unroll
+      for (int qt = 0; qt < 2; qt++) {
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          x[e] = s[qt][0][e];
+          x[4 + e] = s[qt][1][e];
+        }
+        if (need_mask) {
+#pragma unroll
+          for (int e = 0; e < 8; e++) {
+            const int tl = kb * kKBlk + 32 * grp + 8 * g + e;   // key index within the chunk
+            if (tl >= ntok || t0 + tl > qpos[qt]) x[e] = -INFINITY;
+          }
+        }
+        float cmax = x[0];
+#pragma unroll
+        for (int e = 1; e < 8; e++) cmax = fmaxf(cmax, x[e]);
+        cmax *= scale_log2;
+        if (__builtin_amdgcn_ballot_w64(cmax > m_ref[qt] + kLazyRescale)) {
+          const float rmax = row_max(cmax);
+          const float m_new = rmax > m_ref[qt] + kLazyRescale ? rmax : m_ref[qt];
+          const float alpha = m_ref[qt] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref[qt] - m_new);
+          lsum[qt] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < kDv / 16; dt++) o[qt][dt] *= alpha;
+          m_ref[qt] = m_new;
+        }
+        const float mu = m_ref[qt] == -INFINITY ? 0.f : m_ref[qt];
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], scale_log2, -mu));
+          lsum[qt] += p;
+          pb[qt][e] = (__bf16)p;
+        }
+      }
+      // O^T[d][query] += V^T[d][token] . P^T[token][query]: A = 16 dims x 32 tokens of V^T.
+#pragma unroll
+      for (int dt = 0; dt < kDv / 16; dt++) {
+        const bf16x8_t vf = lds_b128(base + v_off(16 * dt + r, 4 * grp + g));
+#pragma unroll
+        for (int qt = 0; qt < 2; qt++) o[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[qt], o[qt][dt], 0, 0, 0);
+      }
+    }
+    if (kb + 1 < nblk) stash((kb + 1) & 1);   // that buffer was last read in block kb-1
+    __syncthreads();
+  }
+
+  // Finalise: lane (g, r) holds O^T[16 dt + 4g + e][query qw + 16 qt + r].
+#pragma unroll
+  for (int qt = 0; qt < 2; qt++) {
+    const float ltot = row_sum(lsum[qt]);
+    const int qi = qw + 16 * qt + r;
+    if (qi >= n) continue;
+    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+    float* orow = out + ((size_t)qi * H + h) * kDv + 4 * g;
+#pragma unroll
+    for (int dt = 0; dt < kDv / 16; dt++) *reinterpret_cast<f32x4_t*>(orow + 16 * dt) = o[qt][dt] * inv;
+    if (g == 0) lse[(size_t)qi * H + h] = ltot > 0.f ? (m_ref[qt] + __builtin_amdgcn_logf(ltot)) * kLn2 : -INFINITY;
+  }
+}
+
+// ===========================================================================
+// LSE merge of J partials
+// ===========================================================================
+constexpr int kMrgThreads = 256;
+constexpr int kMrgRows = kMrgThreads / (kDv / 8);   // 16 rows per workgroup, 8 columns per thread
+
+__global__ __launch_bounds__(kMrgThreads) void mla_lse_merge_kernel(int rows, int J, const float* __restrict__ parts,
+                                                                   const float* __restrict__ lparts,
+                                                                   uint16_t* __restrict__ out, float* __restrict__ lse) {
+  const int row = blockIdx.x * kMrgRows + threadIdx.x / (kDv / 8);
+  const int col = (threadIdx.x % (kDv / 8)) * 8;
+  if (row >= rows) return;
+  float m = -INFINITY, z = 0.f;
+  f32x4_t a0 = f32x4_t{}, a1 = f32x4_t{};
+  for (int j = 0; j < J; j++) {
+    const float lj = lparts[(size_t)j * rows + row];
+    if (lj == -INFINITY) continue;   // no weight; its row is not read
+    const f32x4_t* src = reinterpret_cast<const f32x4_t*>(parts + ((size_t)j * rows + row) * kDv + col);
+    const float m2 = fmaxf(m, lj);
+    const float keep = __expf(m - m2);
+    const float w = __expf(lj - m2);
+    z = z * keep + w;
+    a0 = a0 * keep + w * src[0];
+    a1 = a1 * keep + w * src[1];
+    m = m2;
+  }
+  const float inv = z > 0.f ? 1.f / z : 0.f;
+  bf16x8_t res;
+#pragma unroll
+  for (int e = 0; e < 4; e++) {
+    res[e] = (__bf16)(a0[e] * inv);
+    res[4 + e] = (__bf16)(a1[e] * inv);
+  }
+  *reinterpret_cast<bf16x8_t*>(out + (size_t)row * kDv + col) = res;
+  if (col == 0) lse[row] = z > 0.f ? m + __logf(z) : -INFINITY;
+}
+
+}  // namespace
+
+hipError_t launch_expand_kv(const uint16_t* cache, const int32_t* block_table, int t0, int ntok, int num_pages,
+                            const uint16_t* w_uk, const uint16_t* w_uv, uint16_t* k_out, uint16_t* vt_out, int H,
+                            hipStream_t stream) {
+  int ld = (ntok + 63) / 64 * 64;
+  void* args[] = {(void*)&cache, (void*)&block_table, (void*)&t0,   (void*)&ntok,  (void*)&ld, (void*)&num_pages,
+                  (void*)&w_uk,  (void*)&w_uv,        (void*)&k_out, (void*)&vt_out, (void*)&H};
+  return hipLaunchKernel((const void*)mla_expand_kv_kernel, dim3((ld + kExpTok - 1) / kExpTok, H), dim3(kExpThreads),
+                         args, 0, stream);
+}
+
+hipError_t launch_prefill_attention(const uint16_t* q, const uint16_t* k, const uint16_t* vt, int t0, int ntok, int n,
+                                    int L, int H, float softmax_scale, float* out, float* lse, hipStream_t stream) {
+  int ld = (ntok + 63) / 64 * 64;
+  float scale_log2 = softmax_scale * 1.4426950408889634f;
+  void* args[] = {(void*)&q, (void*)&k, (void*)&vt, (void*)&t0, (void*)&ntok, (void*)&ld, (void*)&n,
+                  (void*)&L, (void*)&H, (void*)&scale_log2, (void*)&out, (void*)&lse};
+  return hipLaunchKernel((const void*)mla_prefill_attention_kernel, dim3((n + kAttQ - 1) / kAttQ, H),
+                         dim3(kAttThreads), args, 0, stream);
+}
+
+hipError_t launch_lse_merge(int rows, int J, const float* parts, const float* lparts, uint16_t* out, float* lse,
+                            hipStream_t stream) {
+  void* args[] = {(void*)&rows, (void*)&J, (void*)&parts, (void*)&lparts, (void*)&out, (void*)&lse};
+  return hipLaunchKernel((const void*)mla_lse_merge_kernel, dim3((rows + kMrgRows - 1) / kMrgRows),
+                         dim3(kMrgThreads), args, 0, stream);
+}
+
+}  // namespace mla

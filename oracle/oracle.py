@@ -194,8 +194,10 @@ def expand_kv(latent, k_rope, w_uk, w_uv):
     """
     latent = np.asarray(latent, dtype=np.float64)
     k_rope = np.asarray(k_rope, dtype=np.float64)
-    k_nope = np.einsum("hnc,tc->htn", np.asarray(w_uk, np.float64), latent)
-    v = np.einsum("hvc,tc->htv", np.asarray(w_uv, np.float64), latent)
+    w_uk = np.asarray(w_uk, np.float64)
+    w_uv = np.asarray(w_uv, np.float64)
+    k_nope = np.stack([latent @ w_uk[h].T for h in range(w_uk.shape[0])])   # [H, T, dn]
+    v = np.stack([latent @ w_uv[h].T for h in range(w_uv.shape[0])])        # [H, T, dv]
     H, T = k_nope.shape[0], k_nope.shape[1]
     k = np.concatenate([k_nope, np.broadcast_to(k_rope[None], (H, T, k_rope.shape[1]))], axis=-1)
     return k, v

@@ -146,3 +146,70 @@ def test_projection_pointers_are_checked(lib):
         assert _status(lambda: M.mla_absorb_q(p, *args)) == M.MLA_ERR_INVALID_ARG, args
     for args in ((0, 16, 16), (16, 0, 16), (16, 16, 0), (16, 32, 40)):
         assert _status(lambda: M.mla_project_out(p, *args)) == M.MLA_ERR_INVALID_ARG, args
+
+
+def _pf_params(**kw):
+    base = dict(num_heads=128, num_new=64, seqlen=1000, num_pages=20, max_blocks=16, chunk_tokens=256)
+    base.update(kw)
+    return M.make_prefill_params(**base)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("num_heads", 0, M.MLA_ERR_INVALID_ARG),
+    ("num_heads", 129, M.MLA_ERR_UNSUPPORTED),
+    ("num_new", 0, M.MLA_ERR_INVALID_ARG),
+    ("num_new", 65537, M.MLA_ERR_INVALID_ARG),
+    ("seqlen", 63, M.MLA_ERR_INVALID_ARG),          # fewer tokens than new tokens
+    ("seqlen", 16 * 64 + 1, M.MLA_ERR_INVALID_ARG),  # more than the block-table row holds
+    ("num_pages", 0, M.MLA_ERR_INVALID_ARG),
+    ("chunk_tokens", 0, M.MLA_ERR_INVALID_ARG),
+    ("chunk_tokens", 100, M.MLA_ERR_INVALID_ARG),
+    ("chunk_tokens", 65600, M.MLA_ERR_INVALID_ARG),
+    ("softmax_scale", 0.0, M.MLA_ERR_INVALID_ARG),
+    ("softmax_scale", float("nan"), M.MLA_ERR_INVALID_ARG),
+    ("d_nope", 64, M.MLA_ERR_UNSUPPORTED),
+    ("d_latent", 256, M.MLA_ERR_UNSUPPORTED),
+])
+def test_bad_prefill_params_are_rejected(lib, field, value, status):
+    p = _pf_params()
+    setattr(p, field, value)
+    assert _status(lambda: M.mla_prefill_workspace_size(p)) == status
+    assert _status(lambda: M.mla_expand_kv(p, 16, 16, 0, 64, 16, 16, 16, 16)) == status
+    assert _status(lambda: M.mla_prefill_attention(p, 16, 16, 16, 0, 64, 16, 16)) == status
+    assert _status(lambda: M.mla_chunked_prefill(p, 16, 16, 16, 16, 16, 256, 1 << 40, 16, 16)) == status
+
+
+def test_prefill_ranges_and_pointers_are_checked(lib):
+    p = _pf_params()
+    for t0, ntok in ((-1, 10), (0, 0), (990, 11), (0, 1001)):
+        assert _status(lambda: M.mla_expand_kv(p, 16, 16, t0, ntok, 16, 16, 16, 16)) == M.MLA_ERR_INVALID_ARG
+        assert _status(lambda: M.mla_prefill_attention(p, 16, 16, 16, t0, ntok, 16, 16)) == M.MLA_ERR_INVALID_ARG
+    for args in ((0, 16, 16, 16, 16, 16), (24, 16, 16, 16, 16, 16), (16, 16, 16, 16, 16, 8)):
+        cache, bt, wuk, wuv, k, vt = args
+        assert _status(lambda: M.mla_expand_kv(p, cache, bt, 0, 64, wuk, wuv, k, vt)) == M.MLA_ERR_INVALID_ARG
+    assert _status(lambda: M.mla_prefill_attention(p, 16, 16, 16, 0, 64, 16, 18)) == M.MLA_ERR_INVALID_ARG
+    # workspace: misaligned, then too small
+    assert _status(lambda: M.mla_chunked_prefill(p, 16, 16, 16, 16, 16, 128, 1 << 40, 16, 16)) == \
+        M.MLA_ERR_INVALID_ARG
+    need = M.mla_prefill_workspace_size(p)
+    assert _status(lambda: M.mla_chunked_prefill(p, 16, 16, 16, 16, 16, 256, need - 1, 16, 16)) == \
+        M.MLA_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_prefill_workspace_covers_every_chunk(lib):
+    """One K and V^T chunk (H x Tc x (192 + 128) bf16) plus fp32 partials and LSEs of all chunks."""
+    p = _pf_params(num_heads=8, num_new=10, seqlen=1000, chunk_tokens=256)
+    need = M.mla_prefill_workspace_size(p)
+    chunks = 4
+    assert need >= 8 * 256 * 320 * 2 + chunks * 10 * 8 * (128 + 1) * 4
+    assert need % 256 == 0
+
+
+@pytest.mark.parametrize("rows,parts", [(0, 1), (1, 0), (1, 4097), (1 << 24 | 1, 2)])
+def test_bad_merge_sizes_are_rejected(lib, rows, parts):
+    assert _status(lambda: M.mla_lse_merge(rows, parts, 16, 16, 16, 16)) == M.MLA_ERR_INVALID_ARG
+
+
+def test_merge_pointers_are_checked(lib):
+    for args in ((0, 16, 16, 16), (8, 16, 16, 16), (16, 18, 16, 16), (16, 16, 8, 16), (16, 16, 16, 2)):
+        assert _status(lambda: M.mla_lse_merge(4, 2, *args)) == M.MLA_ERR_INVALID_ARG

@@ -266,3 +266,46 @@ def make_proj_inputs(*, tokens: int, num_heads: int, seed: int = 0) -> ProjInput
     w_uv = rng.standard_normal((num_heads, D_V, D_LATENT), dtype=np.float32) * np.float32(1 / math.sqrt(D_LATENT))
     return ProjInputs(q_nope=f32_to_bf16_bits(q_nope), q_rope=f32_to_bf16_bits(q_rope), w_uk=f32_to_bf16_bits(w_uk),
                       w_uv=f32_to_bf16_bits(w_uv))
+
+
+@dataclasses.dataclass
+class PrefillWorkload:
+    name: str
+    q: np.ndarray             # uint16 bf16 bits [n, H, 192]  ([q^N ; q^R])
+    cache: np.ndarray         # uint16 bf16 bits [P, 64, 576]  (the request's latents, prefix and new tokens)
+    block_table: np.ndarray   # int32 [max_blocks]  (the request's row)
+    w_uk: np.ndarray          # uint16 bf16 bits [H, 128, 512]
+    w_uv: np.ndarray          # uint16 bf16 bits [H, 128, 512]
+    seqlen: int               # L: tokens in the cache (prefix + new)
+    num_new: int              # n: new tokens, the last n positions
+    num_heads: int
+    softmax_scale: np.float32 = SOFTMAX_SCALE
+
+    @property
+    def num_pages(self) -> int:
+        return int(self.cache.shape[0])
+
+
+def make_prefill_workload(name: str, *, num_heads: int, num_new: int, seqlen: int, seed: int = 0,
+                          spare_pages: int = 2, poison: bool = True) -> PrefillWorkload:
+    """One request for the expand path: its L cached tokens (permuted pages, NaN past its end and in
+    spare pages, as for decode), queries q = [q^N ; q^R] ~ N(0, 1) for the last n positions, and
+    W_UK, W_UV ~ N(0, 1/512) so that k^N = W_UK c and v = W_UV c have the latent's variance."""
+    assert 1 <= num_new <= seqlen
+    wl = make_workload(name, batch=1, num_heads=1, seqlens=[seqlen], seed=seed, spare_pages=spare_pages,
+                       poison=poison)
+    rng = np.random.default_rng(seed + 7919)
+    q = rng.standard_normal((num_new, num_heads, D_NOPE + D_ROPE), dtype=np.float32)
+    w_uk = rng.standard_normal((num_heads, D_NOPE, D_LATENT), dtype=np.float32) * np.float32(1 / math.sqrt(D_LATENT))
+    w_uv = rng.standard_normal((num_heads, D_V, D_LATENT), dtype=np.float32) * np.float32(1 / math.sqrt(D_LATENT))
+    return PrefillWorkload(name=name, q=f32_to_bf16_bits(q), cache=wl.cache, block_table=wl.block_table[0].copy(),
+                           w_uk=f32_to_bf16_bits(w_uk), w_uv=f32_to_bf16_bits(w_uv), seqlen=seqlen,
+                           num_new=num_new, num_heads=num_heads)
+
+
+def prefill_latents(pw: PrefillWorkload) -> tuple[np.ndarray, np.ndarray]:
+    """The request's latent c [L, 512] and RoPE key k^R [L, 64] as float32, gathered through its block table."""
+    L = pw.seqlen
+    rows = pw.cache[pw.block_table[:(L + PAGE - 1) // PAGE]].reshape(-1, D_QK)[:L]
+    x = bf16_bits_to_f32(rows)
+    return x[:, :D_LATENT], x[:, D_LATENT:]
