@@ -8,11 +8,11 @@
 // All contractions run on v_mfma_f32_16x16x32_bf16 with fp32 accumulation.
 //
 // Expansion is a GEMM [tokens x 512] x [512 x (H x 256)] with the latent rows
-// gathered through the block table.  A workgroup owns 128 tokens and one head
-// and stages 64 latent columns at a time of the latent tile and both weight
-// tiles in LDS (double-buffered); waves 0-3 form k^N as C[n][t] (lane holds four
-// consecutive n of one token: 8-byte stores into k[h][t][:]), waves 4-7 form v
-// as C[t][v] (four consecutive tokens of one dim: 8-byte stores into v^T).
+// gathered through the block table.  A workgroup owns 128 tokens, one head and
+// one of the two products, and stages 64 latent columns at a time of the latent
+// tile and the weight tile in LDS (double-buffered): k^N as C[n][t] (a lane
+// holds four consecutive n of one token: 8-byte stores into k[h][t][:]), v as
+// C[t][v] (four consecutive tokens of one dim: 8-byte stores into v^T).
 //
 // Attention keeps the decode kernel's orientation -- scores as S^T = K . q^T,
 // lane = query -- with 32 queries per wave, so every K or V^T fragment read
@@ -63,12 +63,16 @@ __device__ __forceinline__ float row_sum(float x) {
 constexpr int kExpTok = 128;               // tokens per workgroup
 constexpr int kExpC = 64;                  // latent columns per stage
 constexpr int kExpStages = kLat / kExpC;   // 8
-constexpr int kExpThreads = 512;
+constexpr int kExpThreads = 256;
 constexpr int kExpTile = 128 * kExpC * 2;  // 16 KiB: 128 rows x 64 columns, 128-byte rows
 // Row r of a tile: granule j (8 columns) stored at granule j ^ ((r >> 1) & 7), so
 // 16 lanes reading one granule of 16 consecutive rows hit 16 bank groups.
 __device__ __forceinline__ int exp_off(int r, int j) { return r * 128 + ((j ^ ((r >> 1) & 7)) << 4); }
 
+// Workgroup (token tile, head h, which): which = 0 forms k^N as C[n][t] (A = W_UK
+// rows, B = latent rows), which = 1 forms v as C[t][v] (A = latent rows, B = W_UV
+// rows).  Two tiles per stage (64 KiB double-buffered) let two workgroups share
+// a CU and cover each other's load latency.
 __global__ __launch_bounds__(kExpThreads) void mla_expand_kv_kernel(const uint16_t* __restrict__ cache,
                                                                    const int32_t* __restrict__ block_table, int t0,
                                                                    int ntok, int ld, int num_pages,
@@ -76,11 +80,12 @@ __global__ __launch_bounds__(kExpThreads) void mla_expand_kv_kernel(const uint16
                                                                    const uint16_t* __restrict__ w_uv,
                                                                    uint16_t* __restrict__ k_out,
                                                                    uint16_t* __restrict__ vt_out, int H) {
-  // [buffer][lat | W_UK | W_UV]
-  __shared__ __attribute__((aligned(16))) char smem[2 * 3 * kExpTile];
+  // [buffer][latent | weight]
+  __shared__ __attribute__((aligned(16))) char smem[2 * 2 * kExpTile];
   char LDS_AS* lds = (char LDS_AS*)smem;
   const int tile_t = blockIdx.x * kExpTok;   // first token (of the range) of this tile
   const int h = blockIdx.y;
+  const bool is_k = blockIdx.z == 0;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, r = lane & 15;
 
@@ -95,67 +100,68 @@ __global__ __launch_bounds__(kExpThreads) void mla_expand_kv_kernel(const uint16
   };
 
   // k^R: k[h][t][128 .. 191] = cached RoPE key of token t (zeros past the range).
-  for (int i = tid; i < kExpTok * (kRope / 8); i += kExpThreads) {
-    const int j = i >> 3, part = i & 7;
-    if (tile_t + j >= ld) continue;
-    const uint16_t* row = token_row(j);
-    const bf16x8_t v = row ? *reinterpret_cast<const bf16x8_t*>(row + kLat + 8 * part) : bf16x8_t{};
-    *reinterpret_cast<bf16x8_t*>(k_out + ((size_t)h * ld + tile_t + j) * kQK + kNope + 8 * part) = v;
+  if (is_k) {
+    for (int i = tid; i < kExpTok * (kRope / 8); i += kExpThreads) {
+      const int j = i >> 3, part = i & 7;
+      if (tile_t + j >= ld) continue;
+      const uint16_t* row = token_row(j);
+      const bf16x8_t v = row ? *reinterpret_cast<const bf16x8_t*>(row + kLat + 8 * part) : bf16x8_t{};
+      *reinterpret_cast<bf16x8_t*>(k_out + ((size_t)h * ld + tile_t + j) * kQK + kNope + 8 * part) = v;
+    }
   }
 
-  // Stage loads: 3 tiles x 1,024 granules over 512 threads, two granules of each per thread.
-  const uint16_t* lat_row[2];
-  int lr[2], lj[2];
+  // Stage loads: 2 tiles x 1,024 granules over 256 threads, four granules of each per thread.
+  constexpr int kU = 128 * (kExpC / 8) / kExpThreads;   // 4
+  const uint16_t* lat_row[kU];
+  int lr[kU], lj[kU];
 #pragma unroll
-  for (int u = 0; u < 2; u++) {
+  for (int u = 0; u < kU; u++) {
     const int gi = tid + u * kExpThreads;   // 0 .. 1023
     lr[u] = gi >> 3;
     lj[u] = gi & 7;
     lat_row[u] = token_row(lr[u]);
   }
-  const uint16_t* wk = w_uk + (size_t)h * kNope * kLat;
-  const uint16_t* wv = w_uv + (size_t)h * kDv * kLat;
-  bf16x8_t pre[6];
-  auto fetch = [&](int st) {
+  const uint16_t* wt = (is_k ? w_uk : w_uv) + (size_t)h * kNope * kLat;
+  // Stage s is loaded into registers pre[s & 1] two stages ahead and written to LDS
+  // buffer s & 1 at the end of stage s - 1.
+  bf16x8_t pre[2][2 * kU];
+  auto fetch = [&](int st, bf16x8_t (&dst)[2 * kU]) {
     const int c0 = st * kExpC;
 #pragma unroll
-    for (int u = 0; u < 2; u++) {
-      pre[u] = lat_row[u] ? *reinterpret_cast<const bf16x8_t*>(lat_row[u] + c0 + 8 * lj[u]) : bf16x8_t{};
-      pre[2 + u] = *reinterpret_cast<const bf16x8_t*>(wk + (size_t)lr[u] * kLat + c0 + 8 * lj[u]);
-      pre[4 + u] = *reinterpret_cast<const bf16x8_t*>(wv + (size_t)lr[u] * kLat + c0 + 8 * lj[u]);
+    for (int u = 0; u < kU; u++) {
+      dst[u] = lat_row[u] ? *reinterpret_cast<const bf16x8_t*>(lat_row[u] + c0 + 8 * lj[u]) : bf16x8_t{};
+      dst[kU + u] = *reinterpret_cast<const bf16x8_t*>(wt + (size_t)lr[u] * kLat + c0 + 8 * lj[u]);
     }
   };
-  auto stash = [&](int buf) {
-    char LDS_AS* base = lds + buf * 3 * kExpTile;
+  auto stash = [&](int buf, const bf16x8_t (&src)[2 * kU]) {
+    char LDS_AS* base = lds + buf * 2 * kExpTile;
 #pragma unroll
-    for (int u = 0; u < 2; u++) {
+    for (int u = 0; u < kU; u++) {
       const int off = exp_off(lr[u], lj[u]);
-      lds_w128(base + off, pre[u]);
-      lds_w128(base + kExpTile + off, pre[2 + u]);
-      lds_w128(base + 2 * kExpTile + off, pre[4 + u]);
+      lds_w128(base + off, src[u]);
+      lds_w128(base + kExpTile + off, src[kU + u]);
     }
   };
 
-  // Waves 0-3: k^N tile C[n][t] (A = W_UK rows, B = latent rows); waves 4-7: C[t][v]
-  // (A = latent rows, B = W_UV rows).  Each wave owns 64 x 64 of the 128 x 128 tile:
-  // rows 64 (w & 1) + 16 i, columns 64 ((w >> 1) & 1) + 16 j.
-  const bool is_k = wave < 4;
-  const int wq = wave & 3;
-  const int row0 = 64 * (wq & 1), col0 = 64 * (wq >> 1);
-  const int a_tile = is_k ? 1 : 0;   // tile index of the A operand (W_UK or latent)
-  const int b_tile = is_k ? 0 : 2;   // tile index of the B operand (latent or W_UV)
+  // Each wave owns 64 x 64 of the 128 x 128 product: rows 64 (w & 1) + 16 i, columns
+  // 64 (w >> 1) + 16 j.
+  const int row0 = 64 * (wave & 1), col0 = 64 * (wave >> 1);
+  const int a_tile = is_k ? 1 : 0;   // tile index of the A operand (weight or latent)
+  const int b_tile = is_k ? 0 : 1;   // tile index of the B operand (latent or weight)
   f32x4_t acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; i++)
 #pragma unroll
     for (int j = 0; j < 4; j++) acc[i][j] = f32x4_t{};
 
-  fetch(0);
-  stash(0);
+  fetch(0, pre[0]);
+  fetch(1, pre[1]);
+  stash(0, pre[0]);
   __syncthreads();
+#pragma unroll
   for (int st = 0; st < kExpStages; st++) {
-    if (st + 1 < kExpStages) fetch(st + 1);
-    const char LDS_AS* base = lds + (st & 1) * 3 * kExpTile;
+    if (st + 2 < kExpStages) fetch(st + 2, pre[st & 1]);   // stage st's registers were written to LDS already
+    const char LDS_AS* base = lds + (st & 1) * 2 * kExpTile;
 #pragma unroll
     for (int ks = 0; ks < kExpC / 32; ks++) {
       bf16x8_t af[4], bfr[4];
@@ -168,9 +174,7 @@ __global__ __launch_bounds__(kExpThreads) void mla_expand_kv_kernel(const uint16
 #pragma unroll
         for (int j = 0; j < 4; j++) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
-    if (st + 1 < kExpStages) {
-      stash((st + 1) & 1);   // buffer (st+1)&1 was last read in stage st-1, before the barrier below it
-    }
+    if (st + 1 < kExpStages) stash((st + 1) & 1, pre[(st + 1) & 1]);   // last read in stage st-1
     __syncthreads();
   }
 
@@ -233,8 +237,20 @@ __global__ __launch_bounds__(kAttThreads, 2) void mla_prefill_attention_kernel(
     int ntok, int ld, int n, int L, int H, float scale_log2, float* __restrict__ out, float* __restrict__ lse) {
   __shared__ __attribute__((aligned(16))) char smem[2 * kStage];
   char LDS_AS* lds = (char LDS_AS*)smem;
-  const int h = blockIdx.y;
-  const int qb = blockIdx.x * kAttQ;
+  // blockIdx -> (head, query block).  Workgroups are dealt to the 8 XCDs round robin
+  // (linear id % 8); when H is a multiple of 8, head h runs only on XCD h % 8 with
+  // all its query blocks together, so a head's K and V stay in that XCD's L2.
+  // Causal rows late in the sequence see the most keys: they go first, the short
+  // blocks fill the tail.
+  const int nqb = gridDim.x;
+  int h = blockIdx.y, qbi = blockIdx.x;
+  if ((gridDim.y & 7) == 0) {
+    const int lin = blockIdx.x + nqb * blockIdx.y;
+    const int slot = lin >> 3, hh = slot / nqb;
+    qbi = slot - hh * nqb;
+    h = 8 * hh + (lin & 7);
+  }
+  const int qb = (nqb - 1 - qbi) * kAttQ;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, r = lane & 15;
 
@@ -439,8 +455,8 @@ hipError_t launch_expand_kv(const uint16_t* cache, const int32_t* block_table, i
   int ld = (ntok + 63) / 64 * 64;
   void* args[] = {(void*)&cache, (void*)&block_table, (void*)&t0,   (void*)&ntok,  (void*)&ld, (void*)&num_pages,
                   (void*)&w_uk,  (void*)&w_uv,        (void*)&k_out, (void*)&vt_out, (void*)&H};
-  return hipLaunchKernel((const void*)mla_expand_kv_kernel, dim3((ld + kExpTok - 1) / kExpTok, H), dim3(kExpThreads),
-                         args, 0, stream);
+  return hipLaunchKernel((const void*)mla_expand_kv_kernel, dim3((ld + kExpTok - 1) / kExpTok, H, 2),
+                         dim3(kExpThreads), args, 0, stream);
 }
 
 hipError_t launch_prefill_attention(const uint16_t* q, const uint16_t* k, const uint16_t* vt, int t0, int ntok, int n,

@@ -60,3 +60,11 @@ def test_headline_and_mtp_counts():
     assert total == kv + 64 * 128 * (576 * 2 + 512 * 2 + 4) + 64 * 4 + 64 * 64 * 4
     f2, _, _ = bench.workload_counts(np.full(32, 8192), 128, 2, True)
     assert f2 == 32 * (2 * 8192 - 1) * 278528
+
+
+@pytest.mark.parametrize("case", ["prefill 8K", "512 tokens after a 32K prefix"])
+def test_prefill_counts_are_the_handbooks_path_one_totals(golden, case):
+    """bench.py's expand-path FLOPs (expansion of every cached token + causal pairs) reproduce the
+    handbook's path-one totals for these shapes."""
+    c = next(x for x in golden["handbook_flop_script"]["cases_GFLOPs"] if x["name"] == case)
+    assert round(bench.prefill_counts(128, c["q"], c["k"]) / 1e9, 1) == pytest.approx(c["expand"], abs=0.051)
