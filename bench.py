@@ -13,7 +13,8 @@ total at least twice that, unless given).
 Prints one JSON line.  ``value`` is algorithmic TFLOP/s of the whole step;
 ``projections`` times the two per-head projections on either side of the step
 (W_UK absorbed into the query, W_UV on the latent output) separately, and
-``prefill`` the chunked expand path on 512 new tokens after a 32K prefix;
+``prefill`` the chunked expand path on 512 new tokens after a 32K prefix (or,
+with ``--prefill prefill_h128_n8192``, a prefill of 8K new tokens);
 ``roofline`` describes the attention kernel alone (its launches are timed with
 HIP events on the stream it runs on, inside the timed region; the plan and
 combine are timed in a separate pass because each event pair costs GPU time); ``cpu_baseline`` is the fp64 oracle run
@@ -88,6 +89,8 @@ def _parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target duration of the CPU baseline sample")
     ap.add_argument("--no-proj", action="store_true", help="skip the projection kernels' measurement")
     ap.add_argument("--no-prefill", action="store_true", help="skip the expand-path (prefill) measurement")
+    ap.add_argument("--prefill", default="extend_h128_p32768_n512", choices=sorted(PREFILL_WORKLOADS),
+                    help="expand-path workload to measure")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB -> 1 GiB elementwise copy (calibrates the HBM byte counters)")
     return ap.parse_args()
@@ -190,8 +193,11 @@ def bench_projections(torch, M, W, T, H, launches=200):
                       "after the timed region; not part of the step"}
 
 
-PREFILL_WORKLOAD = dict(name="extend_h128_p32768_n512", num_heads=128, num_new=512, seqlen=32768 + 512,
-                        chunk_tokens=8192)
+# The handbook's two expand-path shapes: 512 new tokens after a 32K prefix, and a prefill of 8K new tokens.
+PREFILL_WORKLOADS = {
+    "extend_h128_p32768_n512": dict(num_heads=128, num_new=512, seqlen=32768 + 512, chunk_tokens=8192),
+    "prefill_h128_n8192": dict(num_heads=128, num_new=8192, seqlen=8192, chunk_tokens=8192),
+}
 
 
 def prefill_counts(H, n, L):
@@ -201,13 +207,13 @@ def prefill_counts(H, n, L):
     return L * expand_flops_per_cached_token(H) + causal_pairs(n, L) * pair_flops_expand(H)
 
 
-def bench_prefill(torch, M, W, launches=10):
-    """The chunked expand path (mla_chunked_prefill) on the handbook's "+512 new tokens after a 32K prefix":
-    average time per call over back-to-back calls between one event pair, after the timed region."""
+def bench_prefill(torch, M, W, name, launches=10):
+    """The chunked expand path (mla_chunked_prefill) on one of the handbook's shapes: average time per call
+    over back-to-back calls between one event pair, after the timed region."""
     import numpy as np
-    cfg = PREFILL_WORKLOAD
+    cfg = PREFILL_WORKLOADS[name]
     H, n, L = cfg["num_heads"], cfg["num_new"], cfg["seqlen"]
-    pw = W.make_prefill_workload(cfg["name"], num_heads=H, num_new=n, seqlen=L, seed=1, poison=False)
+    pw = W.make_prefill_workload(name, num_heads=H, num_new=n, seqlen=L, seed=1, poison=False)
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16) if a.dtype == np.uint16 else a).to("cuda")
     q, kv, bt, wuk, wuv = dev(pw.q), dev(pw.cache), dev(pw.block_table), dev(pw.w_uk), dev(pw.w_uv)
     pre = M.MlaPrefill(num_heads=H, num_new=n, seqlen=L, num_pages=pw.num_pages, max_blocks=len(pw.block_table),
@@ -224,7 +230,7 @@ def bench_prefill(torch, M, W, launches=10):
     ms = e0.elapsed_time(e1) / launches
     flops = prefill_counts(H, n, L)
     tflops = flops / (ms * 1e-3) / 1e12
-    return {"workload": cfg["name"], "heads": H, "new_tokens": n, "seqlen": L, "chunk_tokens": cfg["chunk_tokens"],
+    return {"workload": name, "heads": H, "new_tokens": n, "seqlen": L, "chunk_tokens": cfg["chunk_tokens"],
             "ms": round(ms, 4), "gflop": round(flops / 1e9, 1), "tflops": round(tflops, 1),
             "frac_mfma": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
             "timing": f"{launches} back-to-back calls between one event pair, after the timed region; "
@@ -361,7 +367,7 @@ def main():
         del kvs, kss
         line["projections"] = bench_projections(torch, M, W, wl.batch * wl.s_q, wl.num_heads)
     if not args.no_prefill:
-        line["prefill"] = bench_prefill(torch, M, W)
+        line["prefill"] = bench_prefill(torch, M, W, args.prefill)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(line), flush=True)
