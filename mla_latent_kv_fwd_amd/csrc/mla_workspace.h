@@ -14,7 +14,7 @@ namespace mla {
 constexpr int kHeadDimQK = 576;     // 512 latent + 64 RoPE numbers per cached token
 constexpr int kHeadDimV = 512;      // the latent part is the value
 constexpr int kPageSize = 64;       // tokens per page
-constexpr int kRowsPerBlock = 128;  // query rows one workgroup holds (4 waves x 32)
+constexpr int kRowsPerBlock = 128;  // query rows one workgroup holds (8 waves x 16)
 constexpr int kMaxHeads = 128;
 constexpr int kMaxSeqlenQ = 8;
 constexpr int kMaxBatch = 8192;      // requests per step (the plan keeps its arrays in LDS)

@@ -61,7 +61,7 @@ def test_fp8_split_invariance(torch, M, nwg):
     check(out, lse, ref_o, ref_l, f"fp8 nwg={nwg}")
 
 
-@pytest.mark.parametrize("H,s_q", [(16, 1), (64, 2), (128, 2)])
+@pytest.mark.parametrize("H,s_q", [(16, 1), (64, 2), (128, 2), (20, 3), (128, 8)])
 def test_fp8_heads_and_new_tokens(torch, M, H, s_q):
     wl = _fp8(f"fp8h{H}s{s_q}", batch=3, num_heads=H, seqlens=[300, 77, 1500], s_q=s_q, causal=s_q > 1,
               seed=50 + H + s_q, spare_pages=2)

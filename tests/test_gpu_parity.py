@@ -157,7 +157,8 @@ def test_one_token_copies_latent_bits(torch, M):
     check(out, lse, ref_o, ref_l, "one token")
 
 
-@pytest.mark.parametrize("H,s_q", [(16, 1), (32, 1), (64, 1), (128, 2), (64, 2), (16, 2)])
+@pytest.mark.parametrize("H,s_q", [(16, 1), (32, 1), (64, 1), (128, 2), (64, 2), (16, 2), (1, 1), (20, 3), (3, 8),
+                                 (128, 8)])
 def test_head_counts_and_new_tokens(torch, M, H, s_q):
     wl = W.make_workload(f"h{H}s{s_q}", batch=3, num_heads=H, seqlens=[300, 77, 1500], s_q=s_q, causal=s_q > 1,
                          seed=H + s_q, spare_pages=2)
