@@ -8,9 +8,10 @@
 // A piece with lse_j = -inf (a causal row that sees none of that stretch)
 // carries no weight and its output is not read.
 //
-// Memory-bound: one 512-wide fp32 row per piece in, one bf16 row out.  A
-// workgroup of 256 threads handles four rows; each thread owns eight
-// consecutive output columns (two 16-byte loads per piece, two 8-byte stores).  The pieces are merged in one
+// Memory-bound: one 512-wide fp16 row per piece in (stored as O / s with a
+// power-of-two scale s per row), one bf16 row out.  A workgroup of 256 threads
+// handles four rows; each thread owns eight consecutive output columns (one
+// 16-byte load per piece, two 8-byte stores).  The pieces are merged in one
 // online pass (running maximum, normaliser and weighted sum, rescaled when the
 // maximum grows), so the LSEs and partial rows of a group of pieces are all
 // loaded before any of them is used: one memory latency per group instead of
@@ -28,6 +29,7 @@ namespace {
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 
 #define CONST_AS __attribute__((address_space(4)))
 
@@ -64,21 +66,21 @@ __global__ __launch_bounds__(kThreads) void mla_combine_kernel(const char* __res
   if (slot_off < 0 || slot_off + nsplit > max_slots) return;   // never true for a valid plan
   const int rb = row / kRowsPerBlock, rr = row % kRowsPerBlock;
   const float* plse = reinterpret_cast<const float*>(ws + lay.part_lse);
-  const float* pout = reinterpret_cast<const float*>(ws + lay.part_out);
+  const float* pscale = reinterpret_cast<const float*>(ws + lay.part_scale);
+  const _Float16* pout = reinterpret_cast<const _Float16*>(ws + lay.part_out);
   auto pidx = [&](int j) { return ((size_t)(slot_off + j) * nrb + rb) * kRowsPerBlock + rr; };
 
   float m = -INFINITY, z = 0.f;
   f32x4_t acc0 = f32x4_t{}, acc1 = f32x4_t{};
   for (int j0 = 0; j0 < nsplit; j0 += kGroup) {
-    float lj[kGroup];
-    f32x4_t oj0[kGroup], oj1[kGroup];
+    float lj[kGroup], sj[kGroup];
+    f16x8_t oj[kGroup];
 #pragma unroll
     for (int g = 0; g < kGroup; g++) {
       const bool ok = j0 + g < nsplit;
       lj[g] = ok ? plse[pidx(j0 + g)] : -INFINITY;
-      const f32x4_t* src = reinterpret_cast<const f32x4_t*>(pout + pidx(j0 + g) * kHeadDimV + col);
-      oj0[g] = ok ? src[0] : f32x4_t{};
-      oj1[g] = ok ? src[1] : f32x4_t{};
+      sj[g] = ok ? pscale[pidx(j0 + g)] : 0.f;
+      oj[g] = ok ? *reinterpret_cast<const f16x8_t*>(pout + pidx(j0 + g) * kHeadDimV + col) : f16x8_t{};
     }
 #pragma unroll
     for (int g = 0; g < kGroup; g++) {
@@ -86,9 +88,16 @@ __global__ __launch_bounds__(kThreads) void mla_combine_kernel(const char* __res
       const float m2 = fmaxf(m, lj[g]);
       const float keep = __expf(m - m2);  // 0 while m is still -inf
       const float w = __expf(lj[g] - m2);
+      const float ws_ = w * sj[g];   // the piece's weight times its power-of-two scale
       z = z * keep + w;
-      acc0 = acc0 * keep + w * oj0[g];
-      acc1 = acc1 * keep + w * oj1[g];
+      f32x4_t x0, x1;
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        x0[e] = (float)oj[g][e];
+        x1[e] = (float)oj[g][4 + e];
+      }
+      acc0 = acc0 * keep + ws_ * x0;
+      acc1 = acc1 * keep + ws_ * x1;
       m = m2;
     }
   }

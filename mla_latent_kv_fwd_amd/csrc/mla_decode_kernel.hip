@@ -56,6 +56,7 @@ typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef short i16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
 
 #define LDS_AS __attribute__((address_space(3)))
 // Read-only for the whole kernel: reads through this address space become scalar
@@ -187,6 +188,39 @@ __device__ __forceinline__ float row_sum(float x) {
   x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
   r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// A split piece of a row: the normalised output O = o * inv in fp16 as O / s, with s
+// a power of two set from the row's largest |O| so that |O / s| < 2^15, plus s and
+// the LSE.  Lane (q, n) holds dims 16 d + 4q + i of row n; the row's maximum is
+// taken over its four 16-lane groups.
+__device__ __forceinline__ void store_partial(const DecodeArgs& a, size_t pidx, int oq, const f32x4_t (&o)[kDimTiles],
+                                              float inv, float lse_v) {
+  float amax = 0.f;
+#pragma unroll
+  for (int d = 0; d < kDimTiles; d++)
+#pragma unroll
+    for (int r = 0; r < 4; r++) amax = fmaxf(amax, fabsf(o[d][r]));
+  amax = row_max(amax) * inv;
+  // k = 14 - floor(log2 amax), kept where both 2^k and 2^-k are normal floats.
+  const int e = (int)((__float_as_uint(amax) >> 23) & 255) - 127;
+  int k = 14 - e;
+  k = k < -126 ? -126 : (k > 126 ? 126 : k);
+  const float s_inv = __uint_as_float((uint32_t)(127 + k) << 23);
+  const float s = __uint_as_float((uint32_t)(127 - k) << 23);
+  const float f = inv * s_inv;
+  _Float16* prow = reinterpret_cast<_Float16*>(a.ws + a.lay.part_out) + pidx * kHeadDimV + 4 * oq;
+#pragma unroll
+  for (int d = 0; d < kDimTiles; d++) {
+    f16x4_t w;
+#pragma unroll
+    for (int r = 0; r < 4; r++) w[r] = (_Float16)(o[d][r] * f);
+    *reinterpret_cast<f16x4_t*>(prow + 16 * d) = w;
+  }
+  if (oq == 0) {
+    reinterpret_cast<float*>(a.ws + a.lay.part_lse)[pidx] = lse_v;
+    reinterpret_cast<float*>(a.ws + a.lay.part_scale)[pidx] = s;
+  }
 }
 
 __device__ __forceinline__ bf16x8_t lds_read_b128(const char LDS_AS* p) {
@@ -444,10 +478,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
         const int slot_id = rq.slot_off + split;
         if (slot_id < 2 * a.nwg) {
           const size_t pidx = ((size_t)slot_id * a.nrb + rb) * kRowsPerBlock + orow_local;
-          float* prow = reinterpret_cast<float*>(a.ws + a.lay.part_out) + pidx * kHeadDimV + 4 * oq;
-#pragma unroll
-          for (int d = 0; d < kDimTiles; d++) *reinterpret_cast<f32x4_t*>(prow + 16 * d) = o[d] * inv;
-          if (oq == 0) reinterpret_cast<float*>(a.ws + a.lay.part_lse)[pidx] = lse_v;
+          store_partial(a, pidx, oq, o, inv, lse_v);
         }
       }
     }
@@ -783,10 +814,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_fp8_kernel(DecodeArgs 
         const int slot_id = rq.slot_off + split;
         if (slot_id < 2 * a.nwg) {
           const size_t pidx = ((size_t)slot_id * a.nrb + rb) * kRowsPerBlock + orow_local;
-          float* prow = reinterpret_cast<float*>(a.ws + a.lay.part_out) + pidx * kHeadDimV + 4 * oq;
-#pragma unroll
-          for (int d = 0; d < kDimTiles; d++) *reinterpret_cast<f32x4_t*>(prow + 16 * d) = o[d] * inv;
-          if (oq == 0) reinterpret_cast<float*>(a.ws + a.lay.part_lse)[pidx] = lse_v;
+          store_partial(a, pidx, oq, o, inv, lse_v);
         }
       }
     }

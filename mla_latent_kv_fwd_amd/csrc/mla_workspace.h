@@ -54,9 +54,11 @@ struct Header {
   int32_t pad[7];
 };
 
-// Byte offsets of every region; all 256-byte aligned.
+// Byte offsets of every region; all 256-byte aligned.  A split request's piece
+// is stored per row as an LSE, a power-of-two scale s and the normalised output
+// divided by s in fp16 (|O / s| < 2^15: no overflow; the scaling is exact).
 struct Layout {
-  size_t header, wg_info, req_info, part_lse, part_out, total;
+  size_t header, wg_info, req_info, part_lse, part_scale, part_out, total;
 };
 
 MLA_HD inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -71,8 +73,9 @@ MLA_HD inline Layout make_layout(int batch, int rows, int nwg) {
   l.header = off;   off = align256(off + sizeof(Header));
   l.wg_info = off;  off = align256(off + sizeof(WgInfo) * size_t(nwg));
   l.req_info = off; off = align256(off + sizeof(ReqInfo) * size_t(batch));
-  l.part_lse = off; off = align256(off + sizeof(float) * slots * nrb * kRowsPerBlock);
-  l.part_out = off; off = align256(off + sizeof(float) * slots * nrb * kRowsPerBlock * kHeadDimV);
+  l.part_lse = off;   off = align256(off + sizeof(float) * slots * nrb * kRowsPerBlock);
+  l.part_scale = off; off = align256(off + sizeof(float) * slots * nrb * kRowsPerBlock);
+  l.part_out = off;   off = align256(off + sizeof(uint16_t) * slots * nrb * kRowsPerBlock * kHeadDimV);
   l.total = off;
   return l;
 }
