@@ -319,6 +319,11 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
         win += 64;
         pw -= 64;
         win_pages = load_window(win);
+        __builtin_amdgcn_s_waitcnt(VMCNT(0));   // as in the bf16 kernel
+        // Wait here, once per 64 pages: the compiler does not count the
+        // inline-asm chunk loads, so it cannot tell that an older window load
+        // has landed and would otherwise drain every load before each readlane.
+        __builtin_amdgcn_s_waitcnt(VMCNT(0));
       }
       int page = __builtin_amdgcn_readlane(win_pages, pw);
       const bool bad = page < 0 || page >= a.num_pages;
@@ -494,32 +499,37 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
 // and fed to the same bf16 MFMAs; the scale is applied where it is exact in
 // fp32 -- to column t of the scores, and to p_t before P is rounded to bf16 for
 // the P . V product.  The normaliser sums the unscaled p_t.
+//
+// A chunk of 32 tokens arrives as codes in a 4-slot ring (half the bytes of a
+// bf16 chunk, so four chunks are in flight in 74 KiB).  Once it has landed the
+// whole workgroup widens it, in one pass, into one of two bf16 buffers laid out
+// as a bf16 slot; the score and value loops of the bf16 kernel then read it
+// unchanged.  Widening once per chunk costs 1,152 conversions per workgroup,
+// where widening at each read would repeat them in every wave's fragments.
 // ---------------------------------------------------------------------------
 constexpr int kRowBytes8 = kHeadDimQK;                  // 576 one-byte codes per token
 constexpr int kChunk8 = 32;                             // tokens per slot
-constexpr int kSlots8 = 8;                              // ring depth (a slot is half a bf16 slot)
+constexpr int kSlots8 = 4;                              // ring depth (chunks c+1 .. c+4 around iteration c)
 constexpr int kSlotBytes8 = kChunk8 * kRowBytes8;       // 18432
 constexpr int kSlotBlocks8 = kSlotBytes8 / 1024;        // 18 one-KiB loads
 constexpr int kGranPerRow8 = kRowBytes8 / 16;           // 36
 constexpr int kScaleBytes8 = kChunk8 * 4;               // 128 bytes of scales per slot
-constexpr int kLdsBytes8 = kSlots8 * (kSlotBytes8 + kScaleBytes8);
-constexpr int kSuperSteps8 = kHeadDimQK / 64;           // 9 reads of 16 codes per token tile
+constexpr int kRingBytes8 = kSlots8 * (kSlotBytes8 + kScaleBytes8);   // 74,240
+// Widened chunks: two bf16 buffers in the bf16 kernel's slot layout, 1 KiB aligned,
+// then the two chunks' token scales.
+constexpr int kWideOff8 = (kRingBytes8 + 1023) / 1024 * 1024;
+constexpr int kWideScaleOff8 = kWideOff8 + 2 * kSlotBytes;
+constexpr int kLdsBytes8 = kWideScaleOff8 + 2 * kScaleBytes8;
 static_assert(kLdsBytes8 <= 160 * 1024, "FP8 ring must fit in 160 KiB");
 static_assert(kSlotBlocks8 + 1 <= 3 * kWaves, "slot loads (codes + one scale block) fit three per wave");
-
-// XOR swizzle of the low 2 bits of a 576-byte row's 16-byte granule index.
-// Found by a search over linear functions of the token bits under a 64-bank
-// model: it makes both the score read (16 tokens x 16 bytes) and the
-// transposing value read (8 tokens x 16 bytes per 16 lanes) conflict free.
-__device__ __forceinline__ int swz8(int tok) { return ((tok >> 2) & 1) | ((((tok >> 3) ^ (tok >> 4)) & 1) << 1); }
 
 // Loads per wave per slot: 18 code blocks and one scale block over 8 waves.
 __device__ __forceinline__ int dma_per_slot8(int wave) { return wave < 3 ? 3 : 2; }
 
 // Part i of a slot fill: block i*8 + wave.  Blocks 0..17 carry 32 token rows of
-// codes (granule g of the slot is token g / 36, physical granule g % 36 holding
-// logical granule (g % 36) ^ swz8(token)); block 18 carries the 32 scales (8
-// lanes x 4).  Rows at or past `valid` repeat row valid-1.
+// codes in cache order (granule g of the slot is token g / 36, granule g % 36);
+// block 18 carries the 32 scales (8 lanes x 4).  Rows at or past `valid` repeat
+// row valid-1.
 __device__ __forceinline__ void load_chunk_part8(const char* src, const float* scale_src, int valid,
                                                  uint32_t slot_lds, uint32_t scale_lds, int i, int wave, int lane) {
   const int blk = i * kWaves + wave;
@@ -528,7 +538,7 @@ __device__ __forceinline__ void load_chunk_part8(const char* src, const float* s
     const int tok = gi / kGranPerRow8;
     const int phys = gi - tok * kGranPerRow8;
     const int src_tok = tok < valid ? tok : valid - 1;
-    dma16(src, (uint32_t)(src_tok * kRowBytes8 + ((phys ^ swz8(tok)) << 4)), slot_lds + blk * 1024);
+    dma16(src, (uint32_t)(src_tok * kRowBytes8 + (phys << 4)), slot_lds + blk * 1024);
   } else if (blk == kSlotBlocks8 && lane < kChunk8 / 4) {
     dma16(scale_src, (uint32_t)(lane * 16), scale_lds);
   }
@@ -576,21 +586,54 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_fp8_kernel(DecodeArgs 
   const int qi = row_ok ? row / a.num_heads : 0;
   const int ndma = dma_per_slot8(wave);
 
-  // Score read: token 16tt + n, logical granule 4j + q (16 codes: dims
-  // 64j + 16q .. +15) -> physical 4j + (q ^ swz8(token)).
-  const int qk8_off0 = n * kRowBytes8 + ((q ^ swz8(n)) << 4);
-  const int qk8_off1 = (16 + n) * kRowBytes8 + ((q ^ swz8(16 + n)) << 4);
-  // Value read (transposing, 8 tokens x 16 codes per 16 lanes): this lane
-  // supplies row r = (lane & 15) >> 1, i.e. token 4q + (r & 3) + 16 (r >> 2),
-  // and bytes 8 (lane & 1) of granule d (dims 16d .. 16d+15), physical
-  // granule (d & ~3) | ((d & 3) ^ swz8(token)).
-  int pv8_off[4];
+  // Reads of a widened chunk: the bf16 kernel's slot layout and offsets.
+  const int y = q ^ swz(n);
+  const int qk_off0 = n * kRowBytes + ((0 ^ y) << 4);
+  const int qk_off1 = n * kRowBytes + ((4 ^ y) << 4);
+  int pv_off[4];
   {
-    const int r = (lane & 15) >> 1;
-    const int tok = 4 * q + (r & 3) + 16 * (r >> 2);
+    const int tr = 4 * q + ((lane >> 2) & 3);
+    const int z = ((lane >> 1) & 1) ^ swz(tr);
 #pragma unroll
-    for (int dm = 0; dm < 4; dm++) pv8_off[dm] = tok * kRowBytes8 + ((dm ^ swz8(tok)) << 4) + (lane & 1) * 8;
+    for (int dm = 0; dm < 4; dm++) pv_off[dm] = tr * kRowBytes + (((2 * dm) ^ z) << 4) + (lane & 1) * 8;
   }
+
+  // Widening of one chunk by the whole workgroup: 1,152 granules of 16 codes, up
+  // to three per thread (64 consecutive granules per wave read: conflict free).
+  // FP8 granule g of the slot is token g / 36, granule j = g % 36 (dims 16 j ..
+  // +15); its two halves become bf16 logical granules 2 j and 2 j + 1 of the
+  // token's 1,152-byte row, stored at physical granule (logical ^ swz(token)).
+  // The chunk's 32 token scales are copied beside it.
+  auto widen = [&](int cw) {
+    const char LDS_AS* src = smem + (cw % kSlots8) * kSlotBytes8;
+    char LDS_AS* dst = smem + kWideOff8 + (cw & 1) * kSlotBytes;
+    // The thread index, hidden from the optimiser: the addresses below are
+    // recomputed per chunk (a few VALU) instead of kept live across the loop.
+    int tid_o = (int)threadIdx.x;
+    asm volatile("" : "+v"(tid_o));
+#pragma unroll
+    for (int u = 0; u < 3; u++) {
+      const int g = tid_o + kThreads * u;
+      if (g < kSlotBytes8 / 16) {
+        const int tok = g / kGranPerRow8;
+        const int j = g - tok * kGranPerRow8;
+        const i32x4_t w = *reinterpret_cast<const i32x4_t LDS_AS*>(src + 16 * g);
+        bf16x8_t lo, hi;
+        fp8x4_to_bf16((uint32_t)w[0], lo, 0);
+        fp8x4_to_bf16((uint32_t)w[1], lo, 4);
+        fp8x4_to_bf16((uint32_t)w[2], hi, 0);
+        fp8x4_to_bf16((uint32_t)w[3], hi, 4);
+        const int sw = swz(tok);
+        *reinterpret_cast<bf16x8_t LDS_AS*>(dst + tok * kRowBytes + (((2 * j) ^ sw) << 4)) = lo;
+        *reinterpret_cast<bf16x8_t LDS_AS*>(dst + tok * kRowBytes + (((2 * j + 1) ^ sw) << 4)) = hi;
+      }
+    }
+    if (tid_o < kScaleBytes8 / 16) {
+      const f32x4_t v = *reinterpret_cast<const f32x4_t LDS_AS*>(smem + kSlots8 * kSlotBytes8 +
+                                                                 (cw % kSlots8) * kScaleBytes8 + 16 * tid_o);
+      *reinterpret_cast<f32x4_t LDS_AS*>(smem + kWideScaleOff8 + (cw & 1) * kScaleBytes8 + 16 * tid_o) = v;
+    }
+  };
 
   int gpage = wg.page_begin;
   int b = wg.b_begin;
@@ -611,7 +654,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_fp8_kernel(DecodeArgs 
     const int32_t* bt_row = a.block_table + (size_t)b * a.max_blocks;
     const char* kv = reinterpret_cast<const char*>(a.kv);
 
-    // The previous segment's readers of the slots are done.
+    // The previous segment's readers of the slots and buffers are done.
     __syncthreads();
 
     // Block-table window (see the bf16 kernel).
@@ -647,26 +690,22 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_fp8_kernel(DecodeArgs 
     };
     issue(0);
 
-    // Queries, loaded after the first page loads so that both latencies overlap;
-    // one wait covers them all (the compiler tracks only the query loads).
-    // Queries, permuted to match the 16-code reads: fragment 2j + h holds
-    // q~[row][64j + 16q + 8h .. +8), the dims that read j's half h widens to.
+    // Queries (natural order: the widened chunk has the bf16 layout).
     bf16x8_t qf[kKSteps];
     {
       const bf16x8_t* qrow =
-          reinterpret_cast<const bf16x8_t*>(a.q + ((size_t)b * a.rows + (row_ok ? row : 0)) * kHeadDimQK);
+          reinterpret_cast<const bf16x8_t*>(a.q + ((size_t)b * a.rows + (row_ok ? row : 0)) * kHeadDimQK) + q;
 #pragma unroll
-      for (int j = 0; j < kSuperSteps8; j++)
-#pragma unroll
-        for (int h = 0; h < 2; h++) {
-          bf16x8_t v = qrow[8 * j + 2 * q + h];
-          if (!row_ok) v = bf16x8_t{};
-          qf[2 * j + h] = v;
-        }
+      for (int k = 0; k < kKSteps; k++) {
+        bf16x8_t v = qrow[4 * k];
+        if (!row_ok) v = bf16x8_t{};
+        qf[k] = v;
+      }
     }
     __builtin_amdgcn_s_waitcnt(VMCNT(0));
-    // Later chunks land while chunk 0 is processed.
-    for (int c = 1; c < kSlots8 - 1 && c < nchunks; c++) issue(c);
+    for (int c = 1; c < kSlots8 && c < nchunks; c++) issue(c);
+    __syncthreads();   // chunk 0's codes are in LDS
+    widen(0);
 
     float m_ref = -INFINITY;
     float lsum = 0.f;
@@ -675,56 +714,44 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_fp8_kernel(DecodeArgs 
     for (int d = 0; d < kDimTiles; d++) o[d] = f32x4_t{};
 
     for (int c = 0; c < nchunks; c++) {
-      // Wait for this wave's loads of chunk c; up to six later chunks stay in flight.
-      const int ahead = (nchunks - 1 < c + kSlots8 - 2 ? nchunks - 1 : c + kSlots8 - 2) - c;
+      // Wait for this wave's loads of chunk c+1; chunks up to c+3 may stay in flight.
+      const int ahead = c + 1 < nchunks ? (nchunks - 1 < c + 3 ? nchunks - 1 : c + 3) - (c + 1) : 0;
       if (ndma == 3) {
-        switch (ahead) {
-          case 6: __builtin_amdgcn_s_waitcnt(VMCNT(18)); break;
-          case 5: __builtin_amdgcn_s_waitcnt(VMCNT(15)); break;
-          case 4: __builtin_amdgcn_s_waitcnt(VMCNT(12)); break;
-          case 3: __builtin_amdgcn_s_waitcnt(VMCNT(9)); break;
-          case 2: __builtin_amdgcn_s_waitcnt(VMCNT(6)); break;
-          case 1: __builtin_amdgcn_s_waitcnt(VMCNT(3)); break;
-          default: __builtin_amdgcn_s_waitcnt(VMCNT(0)); break;
-        }
+        if (ahead >= 2) __builtin_amdgcn_s_waitcnt(VMCNT(6));
+        else if (ahead == 1) __builtin_amdgcn_s_waitcnt(VMCNT(3));
+        else __builtin_amdgcn_s_waitcnt(VMCNT(0));
       } else {
-        switch (ahead) {
-          case 6: __builtin_amdgcn_s_waitcnt(VMCNT(12)); break;
-          case 5: __builtin_amdgcn_s_waitcnt(VMCNT(10)); break;
-          case 4: __builtin_amdgcn_s_waitcnt(VMCNT(8)); break;
-          case 3: __builtin_amdgcn_s_waitcnt(VMCNT(6)); break;
-          case 2: __builtin_amdgcn_s_waitcnt(VMCNT(4)); break;
-          case 1: __builtin_amdgcn_s_waitcnt(VMCNT(2)); break;
-          default: __builtin_amdgcn_s_waitcnt(VMCNT(0)); break;
-        }
+        if (ahead >= 2) __builtin_amdgcn_s_waitcnt(VMCNT(4));
+        else if (ahead == 1) __builtin_amdgcn_s_waitcnt(VMCNT(2));
+        else __builtin_amdgcn_s_waitcnt(VMCNT(0));
       }
-      __syncthreads();   // chunk c is in LDS everywhere; slot (c-1) % 8 is free
-      if (c + kSlots8 - 1 < nchunks) issue(c + kSlots8 - 1);
+      // Chunk c is widened; chunk c+1's codes are in LDS; slot c % 4 and widened
+      // buffer (c+1) & 1 were last read before this barrier.
+      __syncthreads();
+      if (c + kSlots8 < nchunks) issue(c + kSlots8);
+      if (c + 1 < nchunks) widen(c + 1);
 
-      const int slot_i = c % kSlots8;
-      const char LDS_AS* slot = smem + slot_i * kSlotBytes8;
-      const float LDS_AS* sc_lds = (const float LDS_AS*)(smem + kSlots8 * kSlotBytes8 + slot_i * kScaleBytes8);
+      const char LDS_AS* slot = smem + kWideOff8 + (c & 1) * kSlotBytes;
+      const float LDS_AS* sc_lds = (const float LDS_AS*)(smem + kWideScaleOff8 + (c & 1) * kScaleBytes8);
       const int t0 = t_lo + c * kChunk8;
 
-      // S^T over the 576 dims: each 16-code read widens to two A-fragments.
+      // S^T[token][row] over the 576 dims (the bf16 kernel's loop on the widened chunk).
       f32x4_t s0 = f32x4_t{}, s1 = f32x4_t{};
+      bf16x8_t a0 = lds_read_b128(slot + qk_off0);
+      bf16x8_t a1 = lds_read_b128(slot + 16 * kRowBytes + qk_off0);
 #pragma unroll
-      for (int j = 0; j < kSuperSteps8; j++) {
-        const i32x4_t w0 = *reinterpret_cast<const i32x4_t LDS_AS*>(slot + qk8_off0 + 64 * j);
-        const i32x4_t w1 = *reinterpret_cast<const i32x4_t LDS_AS*>(slot + qk8_off1 + 64 * j);
-        bf16x8_t a0l, a0h, a1l, a1h;
-        fp8x4_to_bf16((uint32_t)w0[0], a0l, 0);
-        fp8x4_to_bf16((uint32_t)w0[1], a0l, 4);
-        fp8x4_to_bf16((uint32_t)w0[2], a0h, 0);
-        fp8x4_to_bf16((uint32_t)w0[3], a0h, 4);
-        fp8x4_to_bf16((uint32_t)w1[0], a1l, 0);
-        fp8x4_to_bf16((uint32_t)w1[1], a1l, 4);
-        fp8x4_to_bf16((uint32_t)w1[2], a1h, 0);
-        fp8x4_to_bf16((uint32_t)w1[3], a1h, 4);
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0l, qf[2 * j], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1l, qf[2 * j], s1, 0, 0, 0);
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0h, qf[2 * j + 1], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1h, qf[2 * j + 1], s1, 0, 0, 0);
+      for (int k = 0; k < kKSteps; k++) {
+        bf16x8_t n0 = a0, n1 = a1;
+        if (k + 1 < kKSteps) {
+          const int off = (((k + 1) & 1) ? qk_off1 : qk_off0) + ((k + 1) >> 1) * 128;
+          n0 = lds_read_b128(slot + off);
+          n1 = lds_read_b128(slot + 16 * kRowBytes + off);
+        }
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[k], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[k], s1, 0, 0, 0);
+        a0 = n0;
+        a1 = n1;
+        __builtin_amdgcn_sched_barrier(0);
       }
 
       // Token scales of this lane's eight tokens: 4q + i and 16 + 4q + i.
@@ -736,9 +763,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_fp8_kernel(DecodeArgs 
         w[i] = i < 4 ? sc0[i] : sc1[i - 4];
         x[i] = (i < 4 ? s0[i] : s1[i - 4]) * w[i];
       }
-      // Keys at or past the row's visible length (a request's last chunk or
-      // causal tail, a uniform branch) get score -inf and weight scale 0: a
-      // scale past a request's end may be anything, NaN included.
+      // Keys at or past the row's visible length get score -inf and weight scale 0
+      // (a scale past a request's end may be anything, NaN included).
       if (t0 + kChunk8 > min_vis) {
         const int lim = n_vis - t0 - 4 * q;
 #pragma unroll
@@ -748,7 +774,6 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_fp8_kernel(DecodeArgs 
             w[i] = 0.f;
           }
       }
-      // Lazy rescale tested on this lane's own maximum (see the bf16 kernel).
       float cmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7]))) *
                    a.scale_log2;
       if (__builtin_amdgcn_ballot_w64(cmax > m_ref + kLazyRescale)) {
@@ -769,23 +794,22 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_fp8_kernel(DecodeArgs 
         pb[i] = (__bf16)(p * w[i]);
       }
 
-      // O^T += V^T . P'^T: one transposing read of 8 tokens x 16 codes per tile.
-      auto read_v8 = [&](int d) {
-        const i32x2_t w = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-            reinterpret_cast<i32x2_t LDS_AS*>(const_cast<char LDS_AS*>(slot) + pv8_off[d & 3] + (d >> 2) * 64));
-        bf16x8_t r;
-        fp8x4_to_bf16((uint32_t)w[0], r, 0);
-        fp8x4_to_bf16((uint32_t)w[1], r, 4);
-        return r;
+      // O^T += V^T . P'^T (the bf16 kernel's loop on the widened chunk).
+      auto read_v = [&](int d) {
+        const int off = pv_off[d & 3] + (d >> 2) * 128;
+        const i16x4_t lo = lds_read_tr16(slot + off);
+        const i16x4_t hi = lds_read_tr16(slot + 16 * kRowBytes + off);
+        return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       };
-      bf16x8_t v0 = read_v8(0), v1 = read_v8(1);
+      bf16x8_t v0 = read_v(0), v1 = read_v(1);
 #pragma unroll
       for (int d = 0; d < kDimTiles; d++) {
         bf16x8_t v2 = v1;
-        if (d + 2 < kDimTiles) v2 = read_v8(d + 2);
+        if (d + 2 < kDimTiles) v2 = read_v(d + 2);
         o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v0, pb, o[d], 0, 0, 0);
         v0 = v1;
         v1 = v2;
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
 
@@ -803,10 +827,10 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_fp8_kernel(DecodeArgs 
           uint16_t* orow = a.out + ((size_t)b * a.rows + orow_g) * kHeadDimV + 4 * oq;
 #pragma unroll
           for (int d = 0; d < kDimTiles; d++) {
-            bf16x4_t w;
+            bf16x4_t wv;
 #pragma unroll
-            for (int r = 0; r < 4; r++) w[r] = (__bf16)(o[d][r] * inv);
-            *reinterpret_cast<bf16x4_t*>(orow + 16 * d) = w;
+            for (int r = 0; r < 4; r++) wv[r] = (__bf16)(o[d][r] * inv);
+            *reinterpret_cast<bf16x4_t*>(orow + 16 * d) = wv;
           }
           if (oq == 0) a.lse[(size_t)b * a.rows + orow_g] = lse_v;
         }
