@@ -16,9 +16,11 @@ Prints one JSON line.  ``value`` is algorithmic TFLOP/s of the whole step;
 ``prefill`` the chunked expand path on 512 new tokens after a 32K prefix (or,
 with ``--prefill prefill_h128_n8192``, a prefill of 8K new tokens);
 ``roofline`` describes the attention kernel alone (its launches are timed with
-HIP events on the stream it runs on, inside the timed region; the plan and
-combine are timed in a separate pass because each event pair costs GPU time); ``cpu_baseline`` is the fp64 oracle run
-on a bounded sample of the same workload's rows on the host cores.
+HIP events on the stream it runs on, inside the timed region, on every 10th
+step; the plan and combine are timed in a separate pass because each event pair
+costs GPU time); ``cpu_baseline`` is the fp64 oracle run on a bounded sample of
+the same workload's rows on the host cores.  Every timed leg starts after the
+GPU has been kept busy for a while, so that its clocks have left the idle state.
 """
 from __future__ import annotations
 
@@ -81,10 +83,14 @@ def workload_counts(seqlens, H, s_q, causal, kv_dtype="bf16"):
 def _parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default=None)
     ap.add_argument("--copies", type=int, default=0, help="independent cache copies to cycle (0 = auto)")
+    ap.add_argument("--event-every", type=int, default=10,
+                    help="record the attention kernel's event pair on every Nth timed step")
+    ap.add_argument("--warm-seconds", type=float, default=WARM_SECONDS,
+                    help="keep the GPU busy this long after the W warm-up steps (0 for counter runs)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target duration of the CPU baseline sample")
     ap.add_argument("--no-proj", action="store_true", help="skip the projection kernels' measurement")
@@ -97,6 +103,25 @@ def _parse():
 
 
 COPY_PROBE_BYTES = 1 << 30
+# Sustained work before any timed region: the GPU's clocks ramp up over the first
+# milliseconds of a burst that starts from idle (measured at the headline shape:
+# ~120 us per step over the first 40 steps after 0.5 s idle, 98-99 us sustained),
+# so a timed region entered from idle clocks would time the ramp, not the kernels.
+WARM_SECONDS = 0.25
+
+
+def keep_busy(torch, fn, seconds=WARM_SECONDS, min_calls=1):
+    """Untimed calls fn(i) until the GPU has run them for `seconds` (host and device kept within 64 calls
+    of each other by periodic synchronisation); returns the number of calls."""
+    calls = 0
+    t0 = time.perf_counter()
+    while calls < min_calls or time.perf_counter() - t0 < seconds:
+        fn(calls)
+        calls += 1
+        if calls % 64 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return calls
 
 
 def copy_probe():
@@ -172,10 +197,8 @@ def bench_projections(torch, M, W, T, H, launches=200):
              "project": lambda z: M.project_out(z[4], z[3], out=z[6])}
     res = {}
     for name, fn in calls.items():
-        for i in range(2 * nsets):
-            fn(sets[i % nsets])
-        torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        keep_busy(torch, lambda i: fn(sets[i % nsets]), seconds=0.1, min_calls=2 * nsets)
         e0.record()
         for i in range(launches):
             fn(sets[i % nsets])
@@ -218,10 +241,8 @@ def bench_prefill(torch, M, W, name, launches=10):
     q, kv, bt, wuk, wuv = dev(pw.q), dev(pw.cache), dev(pw.block_table), dev(pw.w_uk), dev(pw.w_uv)
     pre = M.MlaPrefill(num_heads=H, num_new=n, seqlen=L, num_pages=pw.num_pages, max_blocks=len(pw.block_table),
                        chunk_tokens=cfg["chunk_tokens"])
-    for _ in range(3):
-        pre(q, kv, bt, wuk, wuv)
-    torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    keep_busy(torch, lambda i: pre(q, kv, bt, wuk, wuv), seconds=0.1, min_calls=3)
     e0.record()
     for _ in range(launches):
         pre(q, kv, bt, wuk, wuv)
@@ -295,9 +316,10 @@ def main():
                       softmax_scale=float(wl.softmax_scale))
     stream = torch.cuda.current_stream()
 
-    # Event pairs cost GPU time on this stack (each recorded pair adds a few us to a
-    # step), so the timed region brackets only the attention kernel -- the one the
-    # roofline describes -- and the plan and combine are timed in a separate pass.
+    # Event pairs cost GPU time on this stack (each recorded pair adds several us to
+    # the step it sits in), so inside the timed region only the attention kernel --
+    # the one the roofline describes -- is bracketed, and only on every
+    # --event-every'th step; the plan and combine are timed in a separate pass.
     def step(i, ev=None, all_kernels=False):
         if ev is not None and all_kernels:
             ev[0].record(stream)
@@ -311,19 +333,21 @@ def main():
         if ev is not None and all_kernels:
             ev[3].record(stream)
 
+    every = max(1, args.event_every)
+    evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(4)] for i in range(0, args.steps, every)}
+    # Warm-up: the W steps asked for, then untimed steps until the GPU has been busy
+    # for WARM_SECONDS (clock ramp), ending right before the timed region.
     for i in range(args.warmup):
         step(i)
-    torch.cuda.synchronize()
+    warm_total = args.warmup + keep_busy(torch, lambda i: step(i), seconds=args.warm_seconds, min_calls=0)
 
     # Timed region: exactly `steps` steps, synchronised on both sides.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i, evs[i])
+        step(i, evs.get(i))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    dec_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    dec_ms = [e[1].elapsed_time(e[2]) for e in evs.values()]
 
     # Per-kernel breakdown (outside the timed region): events around every kernel.
     nb = min(args.steps, 50)
@@ -351,6 +375,8 @@ def main():
     line = {
         "metric": "MLA decode TFLOP/s + effective KV GB/s (% roofline), B=64 H=128 L=4096 bf16",
         "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "warmup_note": f"{warm_total} untimed steps in all: the W asked for, then more until the GPU had been "
+                       f"busy {args.warm_seconds} s (clock ramp-up from idle)",
         "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": name, "batch": wl.batch, "heads": wl.num_heads, "seqlen_q": wl.s_q,
@@ -359,7 +385,8 @@ def main():
         "tflops_frac_mfma": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
         "kernel_ms": {"plan": round(float(np.mean(plan_ms)), 5), "decode": round(dec_avg, 5),
                       "combine": round(float(np.mean(comb_ms)), 5)},
-        "kernel_timing": "decode: HIP events inside the timed region; plan, combine: a separate pass after it",
+        "kernel_timing": f"decode: HIP events inside the timed region on every {every}th step "
+                         f"({len(dec_ms)} launches); plan, combine: a separate pass after it",
         "roofline": roof,
         "flags": flags,
     }

@@ -14,7 +14,9 @@
 // One workgroup of 256 threads does the whole plan on the device from the
 // device-resident sequence lengths, so no host synchronisation is needed.  All
 // working arrays live in LDS (batch <= kMaxBatch, stretches <= kMaxStretches),
-// so every binary search is a handful of LDS reads.
+// so every binary search is a handful of LDS reads.  The plan sits on the
+// critical path of every step, so it is written for latency: the lengths are
+// read from global memory once, and each phase costs one or two barriers.
 #include <hip/hip_runtime.h>
 
 #define MLA_HD __host__ __device__
@@ -27,174 +29,199 @@ namespace {
 constexpr int kPlanThreads = 256;
 constexpr int kPlanWaves = kPlanThreads / 64;
 
-// Inclusive scan over the workgroup; `wsum` is scratch for the per-wave totals.
-// Returns the inclusive prefix of this thread; *total receives the block total.
-// Two independent values are scanned together (one set of barriers).
-__device__ int2 block_scan2(int2 v, int2* wsum, int2* total) {
+// Inclusive scan of three values over the workgroup with one pair of barriers;
+// `wsum` is scratch for the per-wave totals.  Returns this thread's inclusive
+// prefixes; *total receives the workgroup totals.
+__device__ int3 block_scan3(int3 v, int3* wsum, int3* total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
-    const int yx = __shfl_up(v.x, off, 64), yy = __shfl_up(v.y, off, 64);
+    const int yx = __shfl_up(v.x, off, 64), yy = __shfl_up(v.y, off, 64), yz = __shfl_up(v.z, off, 64);
     if (lane >= off) {
       v.x += yx;
       v.y += yy;
+      v.z += yz;
     }
   }
   if (lane == 63) wsum[w] = v;
   __syncthreads();
-  int2 pre = make_int2(0, 0), tot = make_int2(0, 0);
+  int3 pre = make_int3(0, 0, 0), tot = make_int3(0, 0, 0);
 #pragma unroll
   for (int i = 0; i < kPlanWaves; i++) {   // a handful of waves: read the totals directly
-    const int2 x = wsum[i];
+    const int3 x = wsum[i];
     if (i < w) {
       pre.x += x.x;
       pre.y += x.y;
+      pre.z += x.z;
     }
     tot.x += x.x;
     tot.y += x.y;
+    tot.z += x.z;
   }
   *total = tot;
   __syncthreads();
-  return make_int2(v.x + pre.x, v.y + pre.y);
-}
-__device__ int block_scan(int v, int2* wsum, int* total) {
-  int2 t;
-  const int2 r = block_scan2(make_int2(v, 0), wsum, &t);
-  *total = t.x;
-  return r.x;
+  return make_int3(v.x + pre.x, v.y + pre.y, v.z + pre.z);
 }
 
-// Largest index i in [0, n) with key(i) <= x, or -1.
+// Largest power of two <= n (n >= 1).
+__device__ int pow2_floor(int n) { return 1 << (31 - __builtin_clz(n)); }
+
+// Largest index i in [0, n) with key(i) <= x, or -1 (key nondecreasing), by
+// binary lifting: one dependent LDS read per halving of the step.
 template <typename F>
 __device__ int last_le(int n, int x, F key) {
-  int lo = 0, hi = n;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (key(mid) <= x) lo = mid + 1; else hi = mid;
-  }
-  return lo - 1;
+  int pos = -1;
+  for (int step = n > 0 ? pow2_floor(n) : 0; step > 0; step >>= 1)
+    if (pos + step < n && key(pos + step) <= x) pos += step;
+  return pos;
+}
+
+// floor(a * b / d) for 0 <= a, b, 0 < d, a * b < 2^53: the double quotient is
+// within one of the exact one, and one integer step on each side corrects it.
+__device__ int floor_muldiv(int a, int b, int d) {
+  const int64_t num = (int64_t)a * b;
+  int64_t q = (int64_t)((double)num / (double)d);
+  if (q * d > num) q--;
+  else if ((q + 1) * d <= num) q++;
+  return (int)q;
 }
 
 __global__ __launch_bounds__(kPlanThreads) void mla_plan_kernel(const int32_t* __restrict__ seqlens, char* ws,
                                                                 Layout lay, int batch, int seqlen_q, int rows,
                                                                 int nwg, int max_blocks) {
-  __shared__ int s_cost[kMaxBatch + 1];   // exclusive prefix of per-request cost
-  __shared__ int s_first[kMaxBatch];      // first page (global position) of each request
-  __shared__ int s_np[kMaxBatch];         // pages of each request
+  __shared__ int s_cost[kMaxBatch];        // exclusive prefix of per-request cost
+  __shared__ int s_first[kMaxBatch];       // first page (global position) of each request
+  __shared__ int s_len[kMaxBatch];         // clamped length of each request
   __shared__ int s_bnd[kMaxStretches + 1];   // stretch boundaries in page positions
+  __shared__ int s_bb[kMaxStretches];        // request that holds each stretch's first page
   __shared__ int s_ne[kMaxStretches + 1];    // non-empty stretches before each stretch
-  __shared__ int2 wsum[kPlanWaves];
-  __shared__ unsigned flags;
+  __shared__ int3 wsum[kPlanWaves];
 
   Header* hdr = reinterpret_cast<Header*>(ws + lay.header);
   WgInfo* wgi = reinterpret_cast<WgInfo*>(ws + lay.wg_info);
   ReqInfo* req = reinterpret_cast<ReqInfo*>(ws + lay.req_info);
   const int t = threadIdx.x;
   const int max_len = max_blocks * kPageSize;
-  if (t == 0) flags = 0;
-  __syncthreads();
+  auto npages_of = [](int L) { return (L + kPageSize - 1) / kPageSize; };
 
-  // 1. pages and cost per request; exclusive prefix sums of both.
-  int carry_p = 0, carry_c = 0;
+  // 1. pages and cost per request; exclusive prefix sums of both, and a count
+  //    of lengths outside [seqlen_q, max_len].
+  int carry_p = 0, carry_c = 0, nbad = 0;
   for (int base = 0; base < batch; base += kPlanThreads) {
     const int b = base + t;
-    int L = 0;
+    int L = 0, bad = 0;
     if (b < batch) {
       L = seqlens[b];
-      if (L < seqlen_q || L > max_len) atomicOr(&flags, 1u);
+      bad = (L < seqlen_q || L > max_len) ? 1 : 0;
       L = L < 0 ? 0 : (L > max_len ? max_len : L);
     }
-    const int np = (L + kPageSize - 1) / kPageSize;
+    const int np = npages_of(L);
     const int cost = np > 0 ? np + kPlanCostPerRequest : 0;
-    int2 tot;
-    const int2 inc = block_scan2(make_int2(np, cost), wsum, &tot);
-    const int inc_p = inc.x, inc_c = inc.y, tot_p = tot.x, tot_c = tot.y;
+    int3 tot;
+    const int3 inc = block_scan3(make_int3(np, cost, bad), wsum, &tot);
     if (b < batch) {
-      s_first[b] = carry_p + inc_p - np;
-      s_np[b] = np;
-      s_cost[b] = carry_c + inc_c - cost;
-      req[b].seqlen = L;
+      s_first[b] = carry_p + inc.x - np;
+      s_cost[b] = carry_c + inc.y - cost;
+      s_len[b] = L;
     }
-    carry_p += tot_p;
-    carry_c += tot_c;
+    carry_p += tot.x;
+    carry_c += tot.y;
+    nbad += tot.z;
   }
   const int total_pages = carry_p;
   const int total_cost = carry_c;
-  if (t == 0) s_cost[batch] = total_cost;
   __syncthreads();
 
-  // 2. stretch boundaries in page positions: boundary s sits at cost s * T / nwg;
-  //    a boundary inside a request's fixed-cost part moves to its first page.
+  // 2. stretch boundaries in page positions: boundary s sits at cost s * T / nwg,
+  //    inside the last request b whose cost range starts at or before it; a
+  //    boundary inside b's fixed-cost part moves to b's first page.  The page
+  //    then lies in [first_b, first_b + np_b), so b also holds it.
   for (int s = t; s <= nwg; s += kPlanThreads) {
-    int bnd;
     if (s == nwg) {
-      bnd = total_pages;
+      s_bnd[s] = total_pages;
     } else {
-      const int x = (int)((int64_t)s * total_cost / nwg);
+      const int x = floor_muldiv(s, total_cost, nwg);
       const int b = last_le(batch, x, [&](int i) { return s_cost[i]; });
+      const int np = npages_of(s_len[b]);
       const int off = x - s_cost[b] - kPlanCostPerRequest;
-      bnd = s_first[b] + (off < 0 ? 0 : (off > s_np[b] ? s_np[b] : off));
+      const int bnd = s_first[b] + (off < 0 ? 0 : (off > np ? np : off));
+      s_bnd[s] = bnd;
+      s_bb[s] = bnd < total_pages ? b : batch;   // no pages at all: every stretch is empty
     }
-    s_bnd[s] = bnd;
   }
   __syncthreads();
 
-  // 3. non-empty stretches: exclusive prefix count, then per-stretch info.
+  // 3. non-empty stretches: exclusive prefix count, written with each stretch's info.
   {
     int carry = 0;
-    for (int base = 0; base <= nwg; base += kPlanThreads) {
+    for (int base = 0; base < nwg; base += kPlanThreads) {
       const int s = base + t;
-      const int ne = (s < nwg && s_bnd[s + 1] > s_bnd[s]) ? 1 : 0;
-      int tot;
-      const int inc = block_scan(ne, wsum, &tot);
-      if (s <= nwg) s_ne[s] = carry + inc - ne;
-      carry += tot;
+      const int pb = s < nwg ? s_bnd[s] : 0;
+      const int pe = s < nwg ? s_bnd[s + 1] : 0;
+      const int ne = pe > pb ? 1 : 0;
+      int3 tot;
+      const int inc = block_scan3(make_int3(ne, 0, 0), wsum, &tot).x;
+      if (s < nwg) {
+        const int ex = carry + inc - ne;
+        s_ne[s] = ex;
+        WgInfo w;
+        w.page_begin = pb;
+        w.page_end = pe;
+        w.b_begin = s_bb[s];
+        w.ne_prefix = ex;
+        wgi[s] = w;
+      }
+      carry += tot.x;
     }
+    if (t == 0) s_ne[nwg] = carry;
   }
   __syncthreads();
-  for (int s = t; s < nwg; s += kPlanThreads) {
-    WgInfo w;
-    w.page_begin = s_bnd[s];
-    w.page_end = s_bnd[s + 1];
-    w.b_begin = w.page_begin < total_pages ? last_le(batch, w.page_begin, [&](int i) { return s_first[i]; }) : batch;
-    w.ne_prefix = s_ne[s];
-    wgi[s] = w;
-  }
 
-  // 4. per request: how many stretches hold it, and its partial slots.
+  // 4. per request: how many stretches hold it, and its partial slots.  The two
+  //    searches (first stretch ending past the request's first page, last stretch
+  //    beginning before its end) run interleaved.
+  const int top = pow2_floor(nwg);
   int carry = 0;
   for (int base = 0; base < batch; base += kPlanThreads) {
     const int b = base + t;
-    int nsplit = 0, ne_lo = 0;
-    if (b < batch && s_np[b] > 0) {
-      const int first = s_first[b], end = first + s_np[b];
-      // first stretch whose end is past the request's first page
-      const int s_lo = 1 + last_le(nwg, first, [&](int i) { return s_bnd[i + 1]; });
-      // last stretch whose begin is before the request's end
-      const int s_hi = last_le(nwg, end - 1, [&](int i) { return s_bnd[i]; });
-      nsplit = s_ne[s_hi + 1] - s_ne[s_lo];
-      ne_lo = s_ne[s_lo];
+    int nsplit = 0, ne_lo = 0, first = 0, L = 0;
+    if (b < batch) {
+      first = s_first[b];
+      L = s_len[b];
+      const int np = npages_of(L);
+      if (np > 0) {
+        const int last = first + np - 1;
+        int lo = -1, hi = -1;
+        for (int step = top; step > 0; step >>= 1) {
+          const int i1 = lo + step, i2 = hi + step;
+          if (i1 < nwg && s_bnd[i1 + 1] <= first) lo = i1;
+          if (i2 < nwg && s_bnd[i2] <= last) hi = i2;
+        }
+        const int s_lo = lo + 1, s_hi = hi;
+        nsplit = s_ne[s_hi + 1] - s_ne[s_lo];
+        ne_lo = s_ne[s_lo];
+      }
     }
     const int slots = nsplit > 1 ? nsplit : 0;
-    int tot;
-    const int inc = block_scan(slots, wsum, &tot);
+    int3 tot;
+    const int inc = block_scan3(make_int3(slots, 0, 0), wsum, &tot).x;
     if (b < batch) {
       ReqInfo r;
-      r.page_first = s_first[b];
-      r.npages = s_np[b];
+      r.page_first = first;
+      r.npages = npages_of(L);
       r.nsplit = nsplit;
       r.slot_off = carry + inc - slots;
       r.ne_lo = ne_lo;
-      r.seqlen = req[b].seqlen;
+      r.seqlen = L;
       r.pad0 = r.pad1 = 0;
       req[b] = r;
     }
-    carry += tot;
+    carry += tot.x;
   }
   if (t == 0) {
     Header h;
     h.magic = kMagic;
-    h.flags = flags;
+    h.flags = nbad > 0 ? 1u : 0u;
     h.batch = batch;
     h.rows = rows;
     h.nwg = nwg;
