@@ -29,38 +29,42 @@ namespace {
 constexpr int kPlanThreads = 256;
 constexpr int kPlanWaves = kPlanThreads / 64;
 
-// Inclusive scan of three values over the workgroup with one pair of barriers;
+// Inclusive scan of four values over the workgroup with one pair of barriers;
 // `wsum` is scratch for the per-wave totals.  Returns this thread's inclusive
 // prefixes; *total receives the workgroup totals.
-__device__ int3 block_scan3(int3 v, int3* wsum, int3* total) {
+__device__ int4 block_scan4(int4 v, int4* wsum, int4* total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
-    const int yx = __shfl_up(v.x, off, 64), yy = __shfl_up(v.y, off, 64), yz = __shfl_up(v.z, off, 64);
+    const int yx = __shfl_up(v.x, off, 64), yy = __shfl_up(v.y, off, 64);
+    const int yz = __shfl_up(v.z, off, 64), yw = __shfl_up(v.w, off, 64);
     if (lane >= off) {
       v.x += yx;
       v.y += yy;
       v.z += yz;
+      v.w += yw;
     }
   }
   if (lane == 63) wsum[w] = v;
   __syncthreads();
-  int3 pre = make_int3(0, 0, 0), tot = make_int3(0, 0, 0);
+  int4 pre = make_int4(0, 0, 0, 0), tot = make_int4(0, 0, 0, 0);
 #pragma unroll
   for (int i = 0; i < kPlanWaves; i++) {   // a handful of waves: read the totals directly
-    const int3 x = wsum[i];
+    const int4 x = wsum[i];
     if (i < w) {
       pre.x += x.x;
       pre.y += x.y;
       pre.z += x.z;
+      pre.w += x.w;
     }
     tot.x += x.x;
     tot.y += x.y;
     tot.z += x.z;
+    tot.w += x.w;
   }
   *total = tot;
   __syncthreads();
-  return make_int3(v.x + pre.x, v.y + pre.y, v.z + pre.z);
+  return make_int4(v.x + pre.x, v.y + pre.y, v.z + pre.z, v.w + pre.w);
 }
 
 // Largest power of two <= n (n >= 1).
@@ -95,7 +99,7 @@ __global__ __launch_bounds__(kPlanThreads) void mla_plan_kernel(const int32_t* _
   __shared__ int s_bnd[kMaxStretches + 1];   // stretch boundaries in page positions
   __shared__ int s_bb[kMaxStretches];        // request that holds each stretch's first page
   __shared__ int s_ne[kMaxStretches + 1];    // non-empty stretches before each stretch
-  __shared__ int3 wsum[kPlanWaves];
+  __shared__ int4 wsum[kPlanWaves];
 
   Header* hdr = reinterpret_cast<Header*>(ws + lay.header);
   WgInfo* wgi = reinterpret_cast<WgInfo*>(ws + lay.wg_info);
@@ -104,21 +108,26 @@ __global__ __launch_bounds__(kPlanThreads) void mla_plan_kernel(const int32_t* _
   const int max_len = max_blocks * kPageSize;
   auto npages_of = [](int L) { return (L + kPageSize - 1) / kPageSize; };
 
-  // 1. pages and cost per request; exclusive prefix sums of both, and a count
-  //    of lengths outside [seqlen_q, max_len].
-  int carry_p = 0, carry_c = 0, nbad = 0;
+  auto clamp_len = [&](int L) { return L < 0 ? 0 : (L > max_len ? max_len : L); };
+  const int np0 = npages_of(clamp_len(seqlens[0]));
+
+  // 1. pages and cost per request; exclusive prefix sums of both, a count of
+  //    lengths outside [seqlen_q, max_len], and a count of requests whose page
+  //    count differs from request 0's (none: every request has the same length).
+  int carry_p = 0, carry_c = 0, nbad = 0, ndiff = 0;
   for (int base = 0; base < batch; base += kPlanThreads) {
     const int b = base + t;
     int L = 0, bad = 0;
     if (b < batch) {
       L = seqlens[b];
       bad = (L < seqlen_q || L > max_len) ? 1 : 0;
-      L = L < 0 ? 0 : (L > max_len ? max_len : L);
+      L = clamp_len(L);
     }
     const int np = npages_of(L);
     const int cost = np > 0 ? np + kPlanCostPerRequest : 0;
-    int3 tot;
-    const int3 inc = block_scan3(make_int3(np, cost, bad), wsum, &tot);
+    const int diff = (b < batch && np != np0) ? 1 : 0;
+    int4 tot;
+    const int4 inc = block_scan4(make_int4(np, cost, bad, diff), wsum, &tot);
     if (b < batch) {
       s_first[b] = carry_p + inc.x - np;
       s_cost[b] = carry_c + inc.y - cost;
@@ -127,15 +136,23 @@ __global__ __launch_bounds__(kPlanThreads) void mla_plan_kernel(const int32_t* _
     carry_p += tot.x;
     carry_c += tot.y;
     nbad += tot.z;
+    ndiff += tot.w;
   }
   const int total_pages = carry_p;
   const int total_cost = carry_c;
   __syncthreads();
 
   // 2. stretch boundaries in page positions: boundary s sits at cost s * T / nwg,
-  //    inside the last request b whose cost range starts at or before it; a
-  //    boundary inside b's fixed-cost part moves to b's first page.  The page
-  //    then lies in [first_b, first_b + np_b), so b also holds it.
+  //    inside the last request b whose cost range starts at or before it.
+  //    Lengths that differ: b's fixed cost sits before its pages, and a boundary
+  //    inside it moves to b's first page (a stretch that takes a short request
+  //    whole pays its set-up once, and no sliver of it is split off).  Equal
+  //    lengths: every request is split the same way and every piece pays its
+  //    own set-up, so b's fixed cost is spread evenly over its pages and the cut
+  //    goes to the page nearest to (s T / nwg - cost_b) * np_b / (np_b + c); with
+  //    the fixed cost in front, the first piece of each request came out c pages
+  //    short (64 pages over four stretches: 13/17/17/17 rather than 16 each).
+  const bool uniform = ndiff == 0;
   for (int s = t; s <= nwg; s += kPlanThreads) {
     if (s == nwg) {
       s_bnd[s] = total_pages;
@@ -143,10 +160,20 @@ __global__ __launch_bounds__(kPlanThreads) void mla_plan_kernel(const int32_t* _
       const int x = floor_muldiv(s, total_cost, nwg);
       const int b = last_le(batch, x, [&](int i) { return s_cost[i]; });
       const int np = npages_of(s_len[b]);
-      const int off = x - s_cost[b] - kPlanCostPerRequest;
-      const int bnd = s_first[b] + (off < 0 ? 0 : (off > np ? np : off));
+      int k;
+      if (uniform) {
+        const double y = (double)s * (double)total_cost / (double)nwg - (double)s_cost[b];
+        k = (int)floor(y * np / (double)(np + kPlanCostPerRequest) + 0.5);
+      } else {
+        k = x - s_cost[b] - kPlanCostPerRequest;
+      }
+      k = k < 0 ? 0 : (k > np ? np : k);
+      const int bnd = s_first[b] + k;
       s_bnd[s] = bnd;
-      s_bb[s] = bnd < total_pages ? b : batch;   // no pages at all: every stretch is empty
+      // The request holding page bnd: b, unless the cut fell at b's end; none
+      // when bnd is past the last page (then the stretch is empty).
+      s_bb[s] = bnd >= total_pages ? batch
+                : (k < np ? b : last_le(batch, bnd, [&](int i) { return s_first[i]; }));
     }
   }
   __syncthreads();
@@ -159,8 +186,8 @@ __global__ __launch_bounds__(kPlanThreads) void mla_plan_kernel(const int32_t* _
       const int pb = s < nwg ? s_bnd[s] : 0;
       const int pe = s < nwg ? s_bnd[s + 1] : 0;
       const int ne = pe > pb ? 1 : 0;
-      int3 tot;
-      const int inc = block_scan3(make_int3(ne, 0, 0), wsum, &tot).x;
+      int4 tot;
+      const int inc = block_scan4(make_int4(ne, 0, 0, 0), wsum, &tot).x;
       if (s < nwg) {
         const int ex = carry + inc - ne;
         s_ne[s] = ex;
@@ -203,8 +230,8 @@ __global__ __launch_bounds__(kPlanThreads) void mla_plan_kernel(const int32_t* _
       }
     }
     const int slots = nsplit > 1 ? nsplit : 0;
-    int3 tot;
-    const int inc = block_scan3(make_int3(slots, 0, 0), wsum, &tot).x;
+    int4 tot;
+    const int inc = block_scan4(make_int4(slots, 0, 0, 0), wsum, &tot).x;
     if (b < batch) {
       ReqInfo r;
       r.page_first = first;

@@ -19,7 +19,7 @@ constexpr int kMaxHeads = 128;
 constexpr int kMaxSeqlenQ = 8;
 constexpr int kMaxBatch = 8192;      // requests per step (the plan keeps its arrays in LDS)
 constexpr int kMaxStretches = 4096;  // persistent workgroups per row block
-constexpr int kPlanCostPerRequest = 2;  // fixed cost of a request segment, in pages
+constexpr int kPlanCostPerRequest = 3;  // fixed cost of a request segment (set-up + finalise), in pages
 constexpr uint32_t kMagic = 0x4D4C4131u;  // "MLA1"
 
 // Per persistent workgroup (stretch) of the plan.

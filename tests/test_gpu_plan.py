@@ -5,14 +5,15 @@ For random length mixes and stretch counts: the stretches partition the
 concatenated pages in order; each request's page range matches its clamped
 length; the stretches holding a request are counted by nsplit and numbered
 0..nsplit-1 by (ne_prefix - ne_lo); split requests get disjoint partial-slot
-ranges inside the reserved 2 * stretches; stretch costs are balanced."""
+ranges inside the reserved 2 * stretches; stretch costs are balanced, and
+equal requests split into equal pieces."""
 import numpy as np
 import pytest
 
 pytestmark = pytest.mark.gpu
 
 PAGE = 64
-COST_PER_REQUEST = 2
+COST_PER_REQUEST = 3
 
 
 def _align(x):
@@ -53,7 +54,7 @@ def _plan(torch, M, seqlens, nwg, max_blocks, s_q=1):
     return hdr, wg, req, nwg_eff
 
 
-@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("seed", range(10))
 def test_plan_invariants(env, seed):
     torch, M = env
     rng = np.random.default_rng(seed)
@@ -62,6 +63,8 @@ def test_plan_invariants(env, seed):
     seqlens = rng.integers(1, max_blocks * PAGE + 1, B)
     if seed % 2:
         seqlens[rng.integers(0, B, max(1, B // 10))] = 1     # sprinkle one-token requests
+    if seed >= 6:
+        seqlens[:] = seqlens[0]                              # equal lengths: the even split
     nwg = int(rng.choice([1, 2, 7, 64, 256, 1000]))
     hdr, wg, req, nwg_eff = _plan(torch, M, seqlens, nwg, max_blocks)
 
@@ -97,14 +100,22 @@ def test_plan_invariants(env, seed):
         assert slots[0][0] >= 0 and slots[-1][1] <= 2 * nwg_eff
     assert hdr[8] == sum(e - s for s, e in slots)           # header.used_slots
 
-    # balance: no stretch costs more than the fair share plus one page and one request's fixed cost
+    # balance: no stretch costs more than the fair share plus one page and one request's
+    # fixed cost.  Lengths that differ: the fixed cost is charged where a request starts;
+    # equal lengths: it is spread over the request's pages (every piece of a split request
+    # pays its own), so a page weighs (np + c) / np and each cut lies within half a page
+    # of its exact cost position
+    uniform = len(set(npages.tolist())) == 1
     cost_of = np.zeros(nwg_eff)
     for s in range(nwg_eff):
         lo, hi = wg[s, 0], wg[s, 1]
         for b in range(B):
             ov = min(hi, first[b] + npages[b]) - max(lo, first[b])
             if ov > 0:
-                cost_of[s] += ov + (COST_PER_REQUEST if lo <= first[b] else 0)
+                if uniform:
+                    cost_of[s] += ov * (npages[b] + COST_PER_REQUEST) / npages[b]
+                else:
+                    cost_of[s] += ov + (COST_PER_REQUEST if lo <= first[b] else 0)
     fair = (total + COST_PER_REQUEST * int((npages > 0).sum())) / nwg_eff
     assert cost_of.max() <= fair + 1 + COST_PER_REQUEST + 1e-9
 
@@ -114,3 +125,13 @@ def test_plan_flags_out_of_range_lengths(env):
     hdr, wg, req, _ = _plan(torch, M, [0, 10_000, 5], nwg=4, max_blocks=4)
     assert hdr[1] & M.MLA_FLAG_SEQLEN_CLAMPED
     assert list(req[:, 5]) == [0, 256, 5] and list(req[:, 1]) == [0, 4, 1]
+
+
+def test_plan_equal_requests_split_evenly(env):
+    """64 requests of 4,096 tokens over 256 stretches: 16 pages each (every piece pays
+    its own fixed cost, so the pieces of equal requests are equal)."""
+    torch, M = env
+    hdr, wg, req, nwg_eff = _plan(torch, M, [4096] * 64, nwg=256, max_blocks=64)
+    assert nwg_eff == 256
+    assert np.all(wg[:, 1] - wg[:, 0] == 16)
+    assert np.all(req[:, 2] == 4)
