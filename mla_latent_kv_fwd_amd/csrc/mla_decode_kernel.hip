@@ -284,9 +284,37 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
   int b = wg.b_begin;
   bool first_segment = true;
   while (gpage < wg.page_end && b < a.batch) {
+    // Set-up of a segment is a chain of memory round trips, so the independent
+    // loads go out together: the queries of request b, the block-table window
+    // (its request-local first page comes from the plan, or is 0 for a later
+    // segment) and the request's info.  Then chunks 0..2 are issued back to back.
+    //
+    // Queries: 18 B-fragments, q~[row][32k + 8q .. +8).
+    bf16x8_t qf[kKSteps];
+    {
+      const bf16x8_t* qrow =
+          reinterpret_cast<const bf16x8_t*>(a.q + ((size_t)b * a.rows + (row_ok ? row : 0)) * kHeadDimQK) + q;
+#pragma unroll
+      for (int k = 0; k < kKSteps; k++) {
+        bf16x8_t v = qrow[4 * k];
+        if (!row_ok) v = bf16x8_t{};
+        qf[k] = v;
+      }
+    }
+    const int pg0 = first_segment ? wg.pg0_local : 0;
+    const int32_t* bt_row = a.block_table + (size_t)b * a.max_blocks;
+    // Block-table window: lane i holds the page of request page pg0 + win + i,
+    // so a chunk's page is one readlane rather than a scalar load waited on.
+    // Entries past the request's pages (within its row) are loaded and unused.
+    auto load_window = [&](int w) {
+      const int pi = pg0 + w + opaque_lane();
+      return pi < a.max_blocks ? bt_row[pi] : 0;
+    };
+    int win = 0;
+    int win_pages = load_window(0);
+
     const ReqInfo rq = load_const<ReqInfo>(reqs + sizeof(ReqInfo) * b);
     if (rq.npages == 0) { b++; continue; }
-    const int pg0 = gpage - rq.page_first;
     const int req_end = rq.page_first + rq.npages;
     const int pg1 = (wg.page_end < req_end ? wg.page_end : req_end) - rq.page_first;
     const int split = first_segment ? wg.ne_prefix - rq.ne_lo : 0;
@@ -296,20 +324,10 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
     const int nchunks = (t_hi - t_lo + kChunk - 1) / kChunk;
     const int n_vis = a.causal ? L - a.seqlen_q + 1 + qi : L;      // keys this lane's row may see
     const int min_vis = a.causal ? L - a.seqlen_q + 1 : L;          // smallest over the request's rows
-    const int32_t* bt_row = a.block_table + (size_t)b * a.max_blocks;
     const char* kv = reinterpret_cast<const char*>(a.kv);
 
     // The previous segment's readers of the slots are done.
     __syncthreads();
-
-    // Block-table window: lane i holds the page of request page pg0 + win + i,
-    // so a chunk's page is one readlane rather than a scalar load waited on.
-    auto load_window = [&](int w) {
-      const int pi = pg0 + w + opaque_lane();
-      return pi < pg1 ? bt_row[pi] : 0;
-    };
-    int win = 0;
-    int win_pages = load_window(0);
 
     auto issue = [&](int c) {
       if (!loader) return;
@@ -319,7 +337,6 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
         win += 64;
         pw -= 64;
         win_pages = load_window(win);
-        __builtin_amdgcn_s_waitcnt(VMCNT(0));   // as in the bf16 kernel
         // Wait here, once per 64 pages: the compiler does not count the
         // inline-asm chunk loads, so it cannot tell that an older window load
         // has landed and would otherwise drain every load before each readlane.
@@ -342,24 +359,11 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
         dma_chunk(src, m0, voff);
       }
     };
-    issue(0);
-
-    // Queries, loaded after the first page loads so that both latencies overlap;
-    // one wait covers them all (the compiler tracks only the query loads).
-    // 18 B-fragments, q~[row][32k + 8q .. +8).
-    bf16x8_t qf[kKSteps];
-    {
-      const bf16x8_t* qrow =
-          reinterpret_cast<const bf16x8_t*>(a.q + ((size_t)b * a.rows + (row_ok ? row : 0)) * kHeadDimQK) + q;
-#pragma unroll
-      for (int k = 0; k < kKSteps; k++) {
-        bf16x8_t v = qrow[4 * k];
-        if (!row_ok) v = bf16x8_t{};
-        qf[k] = v;
-      }
-    }
+    // Queries and window have landed before the first readlane.  Waiting here,
+    // outside the issue loop, leaves the compiler nothing of its own to wait for
+    // inside it, so the chunk loads stay in flight.
     __builtin_amdgcn_s_waitcnt(VMCNT(0));
-    for (int c = 1; c < kSlots - 1 && c < nchunks; c++) issue(c);
+    for (int c = 0; c < kSlots - 1 && c < nchunks; c++) issue(c);
 
     float m_ref = -INFINITY;   // reference maximum (log2 units), same in all lanes of a row
     float lsum = 0.f;          // this lane's part of the normaliser
@@ -639,9 +643,31 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_fp8_kernel(DecodeArgs 
   int b = wg.b_begin;
   bool first_segment = true;
   while (gpage < wg.page_end && b < a.batch) {
+    // Set-up as in the bf16 kernel: queries, block-table window and request
+    // info go out together, then chunks 0..3.
+    // Queries (natural order: the widened chunk has the bf16 layout).
+    bf16x8_t qf[kKSteps];
+    {
+      const bf16x8_t* qrow =
+          reinterpret_cast<const bf16x8_t*>(a.q + ((size_t)b * a.rows + (row_ok ? row : 0)) * kHeadDimQK) + q;
+#pragma unroll
+      for (int k = 0; k < kKSteps; k++) {
+        bf16x8_t v = qrow[4 * k];
+        if (!row_ok) v = bf16x8_t{};
+        qf[k] = v;
+      }
+    }
+    const int pg0 = first_segment ? wg.pg0_local : 0;
+    const int32_t* bt_row = a.block_table + (size_t)b * a.max_blocks;
+    auto load_window = [&](int w) {
+      const int pi = pg0 + w + opaque_lane();
+      return pi < a.max_blocks ? bt_row[pi] : 0;
+    };
+    int win = 0;
+    int win_pages = load_window(0);
+
     const ReqInfo rq = load_const<ReqInfo>(reqs + sizeof(ReqInfo) * b);
     if (rq.npages == 0) { b++; continue; }
-    const int pg0 = gpage - rq.page_first;
     const int req_end = rq.page_first + rq.npages;
     const int pg1 = (wg.page_end < req_end ? wg.page_end : req_end) - rq.page_first;
     const int split = first_segment ? wg.ne_prefix - rq.ne_lo : 0;
@@ -651,19 +677,10 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_fp8_kernel(DecodeArgs 
     const int nchunks = (t_hi - t_lo + kChunk8 - 1) / kChunk8;
     const int n_vis = a.causal ? L - a.seqlen_q + 1 + qi : L;
     const int min_vis = a.causal ? L - a.seqlen_q + 1 : L;
-    const int32_t* bt_row = a.block_table + (size_t)b * a.max_blocks;
     const char* kv = reinterpret_cast<const char*>(a.kv);
 
     // The previous segment's readers of the slots and buffers are done.
     __syncthreads();
-
-    // Block-table window (see the bf16 kernel).
-    auto load_window = [&](int w) {
-      const int pi = pg0 + w + opaque_lane();
-      return pi < pg1 ? bt_row[pi] : 0;
-    };
-    int win = 0;
-    int win_pages = load_window(0);
 
     auto issue = [&](int c) {
       const int t0 = t_lo + c * kChunk8;
@@ -672,6 +689,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_fp8_kernel(DecodeArgs 
         win += 64;
         pw -= 64;
         win_pages = load_window(win);
+        __builtin_amdgcn_s_waitcnt(VMCNT(0));   // as in the bf16 kernel
       }
       int page = __builtin_amdgcn_readlane(win_pages, pw);
       const bool bad = page < 0 || page >= a.num_pages;
@@ -688,22 +706,23 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_fp8_kernel(DecodeArgs 
           load_chunk_part8(src, ssrc, valid, smem_addr + slot * kSlotBytes8, scale_addr + slot * kScaleBytes8, i,
                            wave, lane);
     };
-    issue(0);
-
-    // Queries (natural order: the widened chunk has the bf16 layout).
-    bf16x8_t qf[kKSteps];
+    __builtin_amdgcn_s_waitcnt(VMCNT(0));   // queries and window (as in the bf16 kernel)
+    for (int c = 0; c < kSlots8 && c < nchunks; c++) issue(c);
     {
-      const bf16x8_t* qrow =
-          reinterpret_cast<const bf16x8_t*>(a.q + ((size_t)b * a.rows + (row_ok ? row : 0)) * kHeadDimQK) + q;
-#pragma unroll
-      for (int k = 0; k < kKSteps; k++) {
-        bf16x8_t v = qrow[4 * k];
-        if (!row_ok) v = bf16x8_t{};
-        qf[k] = v;
+      // Wait for this wave's loads of chunk 0; chunks 1..3 may stay in flight.
+      const int after0 = nchunks - 1 < kSlots8 - 1 ? nchunks - 1 : kSlots8 - 1;
+      if (ndma == 3) {
+        if (after0 >= 3) __builtin_amdgcn_s_waitcnt(VMCNT(9));
+        else if (after0 == 2) __builtin_amdgcn_s_waitcnt(VMCNT(6));
+        else if (after0 == 1) __builtin_amdgcn_s_waitcnt(VMCNT(3));
+        else __builtin_amdgcn_s_waitcnt(VMCNT(0));
+      } else {
+        if (after0 >= 3) __builtin_amdgcn_s_waitcnt(VMCNT(6));
+        else if (after0 == 2) __builtin_amdgcn_s_waitcnt(VMCNT(4));
+        else if (after0 == 1) __builtin_amdgcn_s_waitcnt(VMCNT(2));
+        else __builtin_amdgcn_s_waitcnt(VMCNT(0));
       }
     }
-    __builtin_amdgcn_s_waitcnt(VMCNT(0));
-    for (int c = 1; c < kSlots8 && c < nchunks; c++) issue(c);
     __syncthreads();   // chunk 0's codes are in LDS
     widen(0);
 

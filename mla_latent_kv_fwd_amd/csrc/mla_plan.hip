@@ -192,10 +192,13 @@ __global__ __launch_bounds__(kPlanThreads) void mla_plan_kernel(const int32_t* _
         const int ex = carry + inc - ne;
         s_ne[s] = ex;
         WgInfo w;
+        const int bb = s_bb[s];
         w.page_begin = pb;
         w.page_end = pe;
-        w.b_begin = s_bb[s];
+        w.b_begin = bb;
         w.ne_prefix = ex;
+        w.pg0_local = bb < batch ? pb - s_first[bb] : 0;
+        w.pad[0] = w.pad[1] = w.pad[2] = 0;
         wgi[s] = w;
       }
       carry += tot.x;

@@ -28,6 +28,9 @@ struct WgInfo {
   int32_t page_end;    // one past the last page
   int32_t b_begin;     // request that holds page_begin
   int32_t ne_prefix;   // number of non-empty stretches before this one
+  int32_t pg0_local;   // page_begin - page_first of b_begin: lets the decode load the block-table
+                       // window before the request's info arrives (0 for an empty stretch)
+  int32_t pad[3];
 };
 
 // Per request.

@@ -23,7 +23,7 @@ def _align(x):
 def _layout(batch, nwg):
     off = _align(64)                     # header
     wg = off
-    off = _align(off + 16 * nwg)
+    off = _align(off + 32 * nwg)
     req = off
     return wg, req
 
@@ -48,7 +48,7 @@ def _plan(torch, M, seqlens, nwg, max_blocks, s_q=1):
     raw = ws.cpu().numpy()
     nwg_eff = int(raw[16:20].view(np.int32)[0])
     wg_off, req_off = _layout(B, nwg_eff)
-    wg = raw[wg_off:wg_off + 16 * nwg_eff].view(np.int32).reshape(nwg_eff, 4)
+    wg = raw[wg_off:wg_off + 32 * nwg_eff].view(np.int32).reshape(nwg_eff, 8)
     req = raw[req_off:req_off + 32 * B].view(np.int32).reshape(B, 8)
     hdr = raw[:64].view(np.int32)
     return hdr, wg, req, nwg_eff
@@ -93,6 +93,7 @@ def test_plan_invariants(env, seed):
         if nonempty[s]:
             b = wg[s, 2]
             assert first[b] <= wg[s, 0] < first[b] + npages[b]
+            assert wg[s, 4] == wg[s, 0] - first[b]               # request-local first page
     slots.sort()
     for (a0, a1), (b0, _) in zip(slots, slots[1:]):
         assert a1 <= b0
