@@ -9,8 +9,9 @@
 //
 // Expansion is a GEMM [tokens x 512] x [512 x (H x 256)] with the latent rows
 // gathered through the block table.  A workgroup owns 128 tokens, one head and
-// one of the two products, and stages 64 latent columns at a time of the latent
-// tile and the weight tile in LDS (double-buffered): k^N as C[n][t] (a lane
+// one of the two products, and stages 32 latent columns at a time of the latent
+// tile and the weight tile in LDS (double-buffered, 32 KiB, so three workgroups
+// share a CU and cover each other's waits): k^N as C[n][t] (a lane
 // holds four consecutive n of one token: 8-byte stores into k[h][t][:]), v as
 // C[t][v] (four consecutive tokens of one dim: 8-byte stores into v^T).
 //
@@ -61,18 +62,19 @@ __device__ __forceinline__ float row_sum(float x) {
 // Expansion
 // ===========================================================================
 constexpr int kExpTok = 128;               // tokens per workgroup
-constexpr int kExpC = 64;                  // latent columns per stage
-constexpr int kExpStages = kLat / kExpC;   // 8
+constexpr int kExpC = 32;                  // latent columns per stage
+constexpr int kExpStages = kLat / kExpC;   // 16
 constexpr int kExpThreads = 256;
-constexpr int kExpTile = 128 * kExpC * 2;  // 16 KiB: 128 rows x 64 columns, 128-byte rows
-// Row r of a tile: granule j (8 columns) stored at granule j ^ ((r >> 1) & 7), so
+constexpr int kExpTile = 128 * kExpC * 2;  // 8 KiB: 128 rows x 32 columns, 64-byte rows
+// Row r of a tile: granule j (8 columns) stored at granule j ^ ((r >> 2) & 3), so
 // 16 lanes reading one granule of 16 consecutive rows hit 16 bank groups.
-__device__ __forceinline__ int exp_off(int r, int j) { return r * 128 + ((j ^ ((r >> 1) & 7)) << 4); }
+__device__ __forceinline__ int exp_off(int r, int j) { return r * 64 + ((j ^ ((r >> 2) & 3)) << 4); }
 
 // Workgroup (token tile, head h, which): which = 0 forms k^N as C[n][t] (A = W_UK
 // rows, B = latent rows), which = 1 forms v as C[t][v] (A = latent rows, B = W_UV
-// rows).  Two tiles per stage (64 KiB double-buffered) let two workgroups share
-// a CU and cover each other's load latency.
+// rows).  Two 8 KiB tiles per stage, double-buffered (32 KiB), let three
+// workgroups share a CU and cover each other's waits (with 64-column stages and
+// 64 KiB only two fitted: 500 us per 8,192-token chunk against 476 us).
 __global__ __launch_bounds__(kExpThreads) void mla_expand_kv_kernel(const uint16_t* __restrict__ cache,
                                                                    const int32_t* __restrict__ block_table, int t0,
                                                                    int ntok, int ld, int num_pages,
@@ -110,15 +112,15 @@ __global__ __launch_bounds__(kExpThreads) void mla_expand_kv_kernel(const uint16
     }
   }
 
-  // Stage loads: 2 tiles x 1,024 granules over 256 threads, four granules of each per thread.
-  constexpr int kU = 128 * (kExpC / 8) / kExpThreads;   // 4
+  // Stage loads: 2 tiles x 512 granules over 256 threads, two granules of each per thread.
+  constexpr int kU = 128 * (kExpC / 8) / kExpThreads;   // 2
   const uint16_t* lat_row[kU];
   int lr[kU], lj[kU];
 #pragma unroll
   for (int u = 0; u < kU; u++) {
-    const int gi = tid + u * kExpThreads;   // 0 .. 1023
-    lr[u] = gi >> 3;
-    lj[u] = gi & 7;
+    const int gi = tid + u * kExpThreads;   // 0 .. 511
+    lr[u] = gi >> 2;
+    lj[u] = gi & 3;
     lat_row[u] = token_row(lr[u]);
   }
   const uint16_t* wt = (is_k ? w_uk : w_uv) + (size_t)h * kNope * kLat;
