@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 import workloads as W
-from test_gpu_parity import _say, _sampled, check, oracle, run_gpu
+from test_gpu_parity import OUT_MAX_ABS, _say, check, oracle, run_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -89,28 +89,30 @@ def test_fp8_block_table_permutation_is_bit_exact(torch, M):
 
 
 def test_fp8_scale_is_applied_per_token(torch, M):
-    """Doubling every scale of one request doubles its scores (same softmax at half the temperature is
-    not what we check): compare both against the oracle, which takes the scales as given."""
+    """Doubling every scale of one request doubles every cached value: compare both against the oracle, which
+    takes the scales as given.  The doubled cache doubles the outputs and so the bf16 rounding error of each
+    output element (relative 2^-9), so its max-abs bound is the bf16 bound times 2; the relative L2 and LSE
+    bounds are unchanged (the FP8 bar itself is relative L2 <= 3e-2)."""
     wl = _fp8("fp8scale", batch=1, num_heads=16, seqlens=[200], seed=45, spare_pages=1)
     ks = wl.kv_scale.copy()
     ks[np.isfinite(ks)] *= 2.0
     wl2 = W.Workload(name="fp8scale2", q=wl.q, cache=wl.cache, kv_scale=ks, block_table=wl.block_table,
                      seqlens=wl.seqlens, s_q=1, num_heads=16, causal=False)
-    for w in (wl, wl2):
+    for w, factor in ((wl, 1.0), (wl2, 2.0)):
         out, lse, _ = run_gpu(torch, M, w)
         ref_o, ref_l = oracle(w)
-        check(out, lse, ref_o, ref_l, w.name)
+        check(out, lse, ref_o, ref_l, w.name, max_abs=OUT_MAX_ABS * factor)
 
 
-def test_fp8_full_config_sampled_rows(torch, M):
+@pytest.mark.timeout(900)
+def test_fp8_full_config_every_row(torch, M):
+    """The FP8 configuration at full size (128 requests x 16,384 tokens), every output row against the oracle."""
     name = "fp8_b128_h128_l16384"
     _say(f"full config {name}: generating")
     wl = W.make_config(name)
     _say(f"full config {name}: running on GPU")
     out, lse, flags = run_gpu(torch, M, wl)
     assert flags == 0
-    rows = _sampled(wl, 48, seed=5)
-    _say(f"full config {name}: oracle on {len(rows)} rows")
-    ref_o, ref_l = oracle(wl, rows=rows)
-    check(out.reshape(-1, 512)[rows], lse.reshape(-1)[rows], ref_o, ref_l, f"{name} sampled")
-    assert np.isfinite(lse).all()
+    _say(f"full config {name}: oracle on all {wl.batch * wl.num_heads} rows")
+    ref_o, ref_l = oracle(wl)
+    check(out, lse, ref_o, ref_l, f"{name} (whole tensor)")

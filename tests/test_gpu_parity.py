@@ -4,8 +4,9 @@ Tolerances (bf16 inputs, fp32 accumulation): output max-abs <= 2e-2 and relative
 L2 <= 5e-3 over the whole tensor; LSE max-abs <= 1e-3.  Block-table indexing is
 checked bit-exactly (a permuted physical layout of the same logical cache gives
 identical bits), and a one-token request must reproduce its latent's bits.
-Full-size configurations are compared on sampled rows that the oracle computes
-one by one.
+The full-size configurations (headline, ragged batch, two new tokens; the FP8
+cache in test_gpu_fp8.py) are compared on every row of the output, with the
+worst row reported.
 """
 import math
 import os
@@ -75,15 +76,19 @@ def oracle(wl, rows=None):
                     kv_scale=wl.kv_scale, rows=rows)
 
 
-def check(out_bits, lse, ref_out, ref_lse, what):
+def check(out_bits, lse, ref_out, ref_lse, what, max_abs=OUT_MAX_ABS):
     got = W.bf16_bits_to_f32(out_bits).astype(np.float64).reshape(ref_out.shape)
     lse = np.asarray(lse, np.float64).reshape(ref_lse.shape)
     assert np.isfinite(got).all(), f"{what}: non-finite output"
     err = np.abs(got - ref_out)
     rel = np.linalg.norm(got - ref_out) / max(np.linalg.norm(ref_out), 1e-30)
     lerr = np.abs(lse - ref_lse)
-    _say(f"{what}: out max-abs {err.max():.3e} rel-L2 {rel:.3e}  lse max-abs {lerr.max():.3e}")
-    assert err.max() <= OUT_MAX_ABS, f"{what}: out max-abs {err.max()}"
+    d2 = (got - ref_out).reshape(-1, got.shape[-1])
+    r2 = ref_out.reshape(-1, got.shape[-1])
+    row_rel = np.linalg.norm(d2, axis=1) / np.maximum(np.linalg.norm(r2, axis=1), 1e-30)
+    _say(f"{what}: out max-abs {err.max():.3e} rel-L2 {rel:.3e} (worst row {int(row_rel.argmax())}: "
+         f"{row_rel.max():.3e})  lse max-abs {lerr.max():.3e}  [{d2.shape[0]} rows]")
+    assert err.max() <= max_abs, f"{what}: out max-abs {err.max()}"
     assert rel <= OUT_REL_L2, f"{what}: out rel-L2 {rel}"
     assert lerr.max() <= LSE_MAX_ABS, f"{what}: lse max-abs {lerr.max()}"
 
@@ -216,53 +221,80 @@ def test_bad_block_entry_sets_flag_without_fault(torch, M):
     check(out[0:1], lse[0:1], ref_o[0:1], ref_l[0:1], "request beside a bad block entry")
 
 
+def test_workspace_without_matching_plan_sets_flag_without_fault(torch, M):
+    """A workspace that holds no plan, or a plan made for other parameters: the decode reads no plan entry,
+    writes out = 0 and lse = -inf for every row and sets MLA_FLAG_BAD_PLAN; the combine leaves them alone.
+    A matching plan afterwards gives the oracle's result again."""
+    wl = W.make_workload("badplan", batch=3, num_heads=32, seqlens=[300, 77, 1500], seed=9, spare_pages=2)
+    q, kv, _, bt, sl = to_gpu(torch, wl)
+    mk = lambda nwg: M.MlaDecode(batch=3, seqlen_q=1, num_heads=32, num_pages=wl.num_pages,
+                                 max_blocks_per_seq=wl.block_table.shape[1], num_workgroups=nwg)
+    dec, other = mk(5), mk(3)
+    assert other.workspace_bytes <= dec.workspace_bytes
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def run_unplanned():
+        dec.out.fill_(1.0)
+        dec.lse.fill_(1.0)
+        dec.decode(q, kv, bt, sl)
+        dec.combine()
+        torch.cuda.synchronize()
+        assert dec.flags() & M.MLA_FLAG_BAD_PLAN
+        assert (dec.out.float() == 0).all().item()
+        assert torch.isneginf(dec.lse).all().item()
+
+    _say("unplanned workspace")
+    dec.workspace.zero_()                      # never planned
+    run_unplanned()
+    _say("plan for another workgroup count")
+    M.mla_get_workspace(other.params, sl.data_ptr(), dec.workspace.data_ptr(), dec.workspace_bytes, stream)
+    run_unplanned()
+    _say("matching plan")
+    out, lse = dec(q, kv, bt, sl)
+    torch.cuda.synchronize()
+    assert dec.flags() == 0
+    ref_o, ref_l = oracle(wl)
+    check(out.view(torch.int16).cpu().numpy().view(np.uint16), lse.cpu().numpy(), ref_o, ref_l, "after re-plan")
+
+
 def test_out_of_range_seqlen_is_clamped_and_flagged(torch, M):
-    wl = W.make_workload("clamp", batch=2, num_heads=16, seqlens=[100, 100], seed=4)
+    """A length past the block table's reach is clamped to its pages and flagged; a length of 0 gives an empty
+    result.  Request 1 fills its two pages exactly, so every token of the clamped range is finite."""
+    wl = W.make_workload("clamp", batch=2, num_heads=16, seqlens=[100, 128], seed=4)
     sl = wl.seqlens.copy()
-    sl[1] = 100000                       # beyond max_blocks * 64
+    sl[1] = 100000                       # beyond max_blocks * 64 = 128
     sl[0] = 0                            # below s_q: an empty request
     wl2 = W.Workload(name="clamp2", q=wl.q, cache=wl.cache, kv_scale=None, block_table=wl.block_table, seqlens=sl,
                      s_q=1, num_heads=16, causal=False)
     out, lse, flags = run_gpu(torch, M, wl2)
     assert flags & M.MLA_FLAG_SEQLEN_CLAMPED
     assert (out[0] == 0).all() and np.isneginf(lse[0]).all()
-    wl3 = W.Workload(name="clamp3", q=wl.q, cache=wl.cache, kv_scale=None, block_table=wl.block_table,
-                     seqlens=np.array([1, 128], np.int32), s_q=1, num_heads=16, causal=False)
-    ref_o, ref_l = oracle(wl3)                 # 100000 clamps to 2 pages = 128 tokens
-    # the poisoned tail of the original request 1 lies inside the clamped length: compare only finite refs
-    if np.isfinite(ref_o[1]).all():
-        check(out[1:2], lse[1:2], ref_o[1:2], ref_l[1:2], "clamped request")
+    ref_o, ref_l = oracle(wl)                  # 100000 clamps to 2 pages = 128 tokens: the original request 1
+    assert np.isfinite(ref_o[1]).all()
+    check(out[1:2], lse[1:2], ref_o[1:2], ref_l[1:2], "clamped request")
 
 
-# ------------------------------------------------------------------ full-size configurations, sampled rows
-def _sampled(wl, nrows, seed):
-    rng = np.random.default_rng(seed)
-    total = wl.batch * wl.s_q * wl.num_heads
-    rows = np.unique(np.concatenate([rng.integers(0, total, nrows), [0, total - 1]]))
-    return rows
-
-
+# ------------------------------------------------------------------ full-size configurations, every row
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["dsv3_b64_h128_l4096", "ragged_b128_h128_l128_32768", "mtp_b32_h128_sq2_l8192"])
-def test_full_config_sampled_rows(torch, M, name):
+def test_full_config_every_row(torch, M, name):
+    """The measured configurations at full size, every output row against the oracle (relative L2 over the
+    whole tensor, the worst row reported)."""
     _say(f"full config {name}: generating")
     wl = W.make_config(name)
     _say(f"full config {name}: running on GPU")
     out, lse, flags = run_gpu(torch, M, wl)
     assert flags == 0
-    rows = _sampled(wl, 96, seed=len(name))
-    _say(f"full config {name}: oracle on {len(rows)} rows")
-    ref_o, ref_l = oracle(wl, rows=rows)
-    got_o = out.reshape(-1, 512)[rows]
-    got_l = lse.reshape(-1)[rows]
-    check(got_o, got_l, ref_o, ref_l, f"{name} sampled")
-    # properties that hold at any size: every row finite, LSE above the log of nothing
-    assert np.isfinite(lse).all()
+    _say(f"full config {name}: oracle on all {wl.batch * wl.s_q * wl.num_heads} rows")
+    ref_o, ref_l = oracle(wl)
+    check(out, lse, ref_o, ref_l, f"{name} (whole tensor)")
 
 
+@pytest.mark.timeout(600)
 def test_single_long_request_split_everywhere(torch, M):
     """One 131,072-token request: every persistent workgroup holds a piece; the combine merges 256 pieces."""
     wl = W.make_workload("long1", batch=1, num_heads=128, seqlens=[131072], seed=8)
+    _say("131072-token request")
     out, lse, _ = run_gpu(torch, M, wl)
-    rows = _sampled(wl, 24, seed=1)
-    ref_o, ref_l = oracle(wl, rows=rows)
-    check(out.reshape(-1, 512)[rows], lse.reshape(-1)[rows], ref_o, ref_l, "131072-token request")
+    ref_o, ref_l = oracle(wl)
+    check(out, lse, ref_o, ref_l, "131072-token request (every row)")

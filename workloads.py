@@ -10,8 +10,14 @@ the handbook page "MLA inference: two computation paths and FlashMLA" gives
 them in "Which is faster" and in its FlashMLA paragraph.
 
 Recipe (fixed so any run can be reproduced):
-  * RNG: numpy ``default_rng(seed)`` (PCG64); draw order: seqlens (ragged only)
-    -> page permutation -> q~ -> cache latent -> cache RoPE part.
+  * RNG: numpy ``default_rng(seed)`` (PCG64); draw order on it: seqlens
+    (ragged only) -> page permutation -> one 63-bit root seed for the values.
+  * The values come from PCG64 streams spawned from that root
+    (``SeedSequence(root).spawn``): stream b draws request b's queries
+    [s_q, H, 576]; stream B + j draws the latent [n, 64, 512] and then the RoPE
+    part [n, 64, 64] of pages 64 j .. 64 j + n - 1 (physical page order).  The
+    streams are independent, so blocks are drawn on several threads at once and
+    encoded straight into the stored format (no whole-cache float32 copy).
   * Values are drawn in float32 and stored as bf16 with round-to-nearest-even;
     the FP8 cache stores OCP E4M3FN codes of x / s_t with a per-token scale
     s_t = amax_t / 448 over all 576 numbers of the token (1 when amax is 0).
@@ -21,8 +27,10 @@ Recipe (fixed so any run can be reproduced):
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
 import math
+import os
 from typing import Optional, Sequence
 
 import numpy as np
@@ -100,6 +108,28 @@ def _normal_f32(rng: np.random.Generator, shape, chunk_rows: int = 1 << 20) -> n
     return out
 
 
+PAGES_PER_STREAM = 64   # pages drawn from one spawned value stream
+_WORKERS = max(1, min(16, os.cpu_count() or 1))
+
+
+def _parallel(fn, n):
+    """fn(i) for i < n on a thread pool (numpy's fills and ufuncs release the GIL)."""
+    if n <= 1 or _WORKERS == 1:
+        for i in range(n):
+            fn(i)
+        return
+    with concurrent.futures.ThreadPoolExecutor(_WORKERS) as ex:
+        for f in [ex.submit(fn, i) for i in range(n)]:
+            f.result()
+
+
+def _encode_fp8_tokens(x: np.ndarray):
+    """Per-token scale s = amax / 448 over the last axis (1 when amax is 0) and the E4M3FN codes of x / s."""
+    amax = np.abs(x).max(axis=-1)
+    s = np.where(amax > 0, amax / np.float32(E4M3FN_MAX), np.float32(1.0)).astype(np.float32)
+    return f32_to_e4m3fn(x / s[..., None]), s
+
+
 def make_workload(name: str, *, batch: int, num_heads: int, seqlens: Sequence[int] | np.ndarray, s_q: int = 1,
                   causal: bool = False, seed: int = 0, latent_std: float = 1.0, q_std: float = 1.0,
                   rope_std: float = 1.0, kv_dtype: str = "bf16", permute_pages: bool = True,
@@ -109,8 +139,10 @@ def make_workload(name: str, *, batch: int, num_heads: int, seqlens: Sequence[in
 
     ``shape_values(q, latent, rope, block_table, seqlens, rng)``, if given, may
     rewrite the float32 draws in place before they are encoded (structured
-    inputs for a test).
+    inputs for a test; the whole cache is then held in float32 once).
     """
+    if kv_dtype not in ("bf16", "fp8_e4m3fn"):
+        raise ValueError(kv_dtype)
     rng = np.random.default_rng(seed) if rng is None else rng
     seqlens = np.asarray(seqlens, dtype=np.int32)
     assert seqlens.shape == (batch,) and (seqlens >= s_q).all()
@@ -127,39 +159,64 @@ def make_workload(name: str, *, batch: int, num_heads: int, seqlens: Sequence[in
         block_table[b, :npages[b]] = perm[off:off + npages[b]]
         off += int(npages[b])
 
-    q = _normal_f32(rng, (batch, s_q, num_heads, D_QK))
-    if q_std != 1.0:
-        q *= np.float32(q_std)
-    latent = _normal_f32(rng, (P, PAGE, D_LATENT))
-    if latent_std != 1.0:
-        latent *= np.float32(latent_std)
-    rope = _normal_f32(rng, (P, PAGE, D_ROPE))
-    if rope_std != 1.0:
-        rope *= np.float32(rope_std)
-    if shape_values is not None:
-        shape_values(q, latent, rope, block_table, seqlens, rng)
-    q_bits = f32_to_bf16_bits(q)
-    del q
+    nblk = (P + PAGES_PER_STREAM - 1) // PAGES_PER_STREAM
+    streams = np.random.SeedSequence(int(rng.integers(0, 1 << 63))).spawn(batch + nblk)
+    gen = lambda i: np.random.Generator(np.random.PCG64(streams[i]))
 
-    kv_scale = None
-    if kv_dtype == "bf16":
-        cache = np.empty((P, PAGE, D_QK), dtype=np.uint16)
-        cache[..., :D_LATENT] = f32_to_bf16_bits(latent)
-        cache[..., D_LATENT:] = f32_to_bf16_bits(rope)
-    elif kv_dtype == "fp8_e4m3fn":
-        cache = np.empty((P, PAGE, D_QK), dtype=np.uint8)
-        kv_scale = np.empty((P, PAGE), dtype=np.float32)
-        step = 1024
-        for p0 in range(0, P, step):
-            p1 = min(P, p0 + step)
-            x = np.concatenate([latent[p0:p1], rope[p0:p1]], axis=-1)
-            amax = np.abs(x).max(axis=-1)
-            s = np.where(amax > 0, amax / np.float32(E4M3FN_MAX), np.float32(1.0)).astype(np.float32)
-            kv_scale[p0:p1] = s
-            cache[p0:p1] = f32_to_e4m3fn(x / s[..., None])
+    q_bits = np.empty((batch, s_q, num_heads, D_QK), dtype=np.uint16)
+    q32 = np.empty((batch, s_q, num_heads, D_QK), dtype=np.float32) if shape_values is not None else None
+
+    def draw_q(b):
+        x = gen(b).standard_normal((s_q, num_heads, D_QK), dtype=np.float32)
+        if q_std != 1.0:
+            x *= np.float32(q_std)
+        if q32 is not None:
+            q32[b] = x
+        else:
+            q_bits[b] = f32_to_bf16_bits(x)
+
+    def draw_pages(j):
+        p0 = j * PAGES_PER_STREAM
+        n = min(P, p0 + PAGES_PER_STREAM) - p0
+        g = gen(batch + j)
+        lat = g.standard_normal((n, PAGE, D_LATENT), dtype=np.float32)
+        rope = g.standard_normal((n, PAGE, D_ROPE), dtype=np.float32)
+        if latent_std != 1.0:
+            lat *= np.float32(latent_std)
+        if rope_std != 1.0:
+            rope *= np.float32(rope_std)
+        return p0, n, lat, rope
+
+    kv_scale = np.empty((P, PAGE), dtype=np.float32) if kv_dtype == "fp8_e4m3fn" else None
+    cache = np.empty((P, PAGE, D_QK), dtype=np.uint16 if kv_dtype == "bf16" else np.uint8)
+
+    def encode(p0, n, lat, rope):
+        if kv_dtype == "bf16":
+            cache[p0:p0 + n, :, :D_LATENT] = f32_to_bf16_bits(lat)
+            cache[p0:p0 + n, :, D_LATENT:] = f32_to_bf16_bits(rope)
+        else:
+            cache[p0:p0 + n], kv_scale[p0:p0 + n] = _encode_fp8_tokens(np.concatenate([lat, rope], axis=-1))
+
+    if shape_values is None:
+        _parallel(draw_q, batch)
+        _parallel(lambda j: encode(*draw_pages(j)), nblk)
     else:
-        raise ValueError(kv_dtype)
-    del latent, rope
+        latent = np.empty((P, PAGE, D_LATENT), dtype=np.float32)
+        rope_all = np.empty((P, PAGE, D_ROPE), dtype=np.float32)
+
+        def fill(j):
+            p0, n, lat, rope = draw_pages(j)
+            latent[p0:p0 + n] = lat
+            rope_all[p0:p0 + n] = rope
+
+        _parallel(draw_q, batch)
+        _parallel(fill, nblk)
+        shape_values(q32, latent, rope_all, block_table, seqlens, rng)
+        q_bits[...] = f32_to_bf16_bits(q32)
+        _parallel(lambda j: encode(j * PAGES_PER_STREAM, min(P, (j + 1) * PAGES_PER_STREAM) - j * PAGES_PER_STREAM,
+                                   latent[j * PAGES_PER_STREAM:(j + 1) * PAGES_PER_STREAM],
+                                   rope_all[j * PAGES_PER_STREAM:(j + 1) * PAGES_PER_STREAM]), nblk)
+        del latent, rope_all, q32
 
     if poison:
         nan = BF16_NAN if kv_dtype == "bf16" else E4M3FN_NAN
