@@ -39,7 +39,8 @@
  *  - Device-side values are not validated synchronously (that would need a host
  *    sync).  The kernels never read outside the buffers the parameters describe:
  *    sequence lengths are clamped to [0, max_blocks_per_seq * page_size], and a
- *    block-table entry outside [0, num_pages) is not dereferenced.  Either event
+ *    block-table entry outside [0, num_pages) is not dereferenced, and a plan
+ *    is used only if its header matches the call's parameters.  Each event
  *    sets a bit in the workspace that mla_workspace_flags() reports.
  *  - Calls on distinct workspaces may run concurrently; calls sharing a
  *    workspace must be ordered on one stream.
@@ -73,6 +74,9 @@ typedef enum {
 /* Bits reported by mla_workspace_flags(). */
 #define MLA_FLAG_SEQLEN_CLAMPED 0x1  /* some seqlens[b] was < seqlen_q or > max_blocks_per_seq * page_size */
 #define MLA_FLAG_BAD_BLOCK      0x2  /* some referenced block-table entry was outside [0, num_pages) */
+#define MLA_FLAG_BAD_PLAN       0x4  /* the workspace holds no plan, or one made for other parameters (batch,
+                                        seqlen_q * num_heads, workgroup count or max_blocks_per_seq): the decode
+                                        wrote out = 0 and lse = -inf for every row and read nothing else */
 
 typedef struct {
   int32_t batch;               /* B >= 1: requests in the step */

@@ -17,7 +17,9 @@ import math
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libmla_decode.so")
+# MLA_DECODE_LIB selects another build of the same library (the host-sanitizer build that
+# tests/test_sanitizers.py makes); by default the in-tree library.
+LIB_PATH = os.environ.get("MLA_DECODE_LIB") or os.path.join(_PKG, "libmla_decode.so")
 
 MLA_OK = 0
 MLA_ERR_INVALID_ARG = -1
@@ -28,6 +30,7 @@ MLA_KV_BF16 = 0
 MLA_KV_FP8_E4M3FN = 1
 MLA_FLAG_SEQLEN_CLAMPED = 0x1
 MLA_FLAG_BAD_BLOCK = 0x2
+MLA_FLAG_BAD_PLAN = 0x4
 
 HEAD_DIM_QK = 576
 HEAD_DIM_V = 512
@@ -278,6 +281,61 @@ class MlaPrefill:
         return out, lse
 
 
+def _resolve_device(device):
+    """torch.device with the index filled in ("cuda" -> the current HIP device)."""
+    import torch
+    dev = torch.device(device)
+    if dev.type == "cuda" and dev.index is None:
+        dev = torch.device("cuda", torch.cuda.current_device())
+    return dev
+
+
+def check_decode_inputs(params: DecodeParams, device, q, kv_cache, block_table, seqlens, kv_scale=None) -> None:
+    """Raise ValueError unless the tensors match what mla_decode_fwd reads for these parameters:
+    q a contiguous 16-bit [B, s_q, H, 576]; kv_cache a contiguous [num_pages, 64, 576] of 16-bit values (bf16)
+    or bytes (E4M3FN codes); kv_scale a contiguous float32 [num_pages, 64] exactly when the cache is FP8;
+    block_table a contiguous int32 [B, max_blocks_per_seq]; seqlens a contiguous int32 [B]; all on `device`.
+    The kernels index these buffers by the parameters alone, so a smaller or differently typed tensor would be
+    read out of bounds."""
+    import torch
+    p = params
+    B, s_q, H = p.batch, p.seqlen_q, p.num_heads
+    fp8 = p.kv_dtype == MLA_KV_FP8_E4M3FN
+
+    def need(cond, msg):
+        if not cond:
+            raise ValueError(msg)
+
+    dev = _resolve_device(device)
+
+    def on_dev(x, name):
+        need(x.device == dev, f"{name}: on {x.device}, expected {dev}")
+        need(x.is_contiguous(), f"{name}: must be contiguous")
+
+    need(tuple(q.shape) == (B, s_q, H, HEAD_DIM_QK) and q.element_size() == 2,
+         f"q: expected a 16-bit [{B}, {s_q}, {H}, {HEAD_DIM_QK}] tensor, got {q.dtype} {tuple(q.shape)}")
+    on_dev(q, "q")
+    kv_shape = (p.num_pages, PAGE_SIZE, HEAD_DIM_QK)
+    if fp8:
+        need(tuple(kv_cache.shape) == kv_shape and kv_cache.element_size() == 1,
+             f"kv_cache: expected 1-byte E4M3FN codes of shape {kv_shape}, got {kv_cache.dtype} {tuple(kv_cache.shape)}")
+        need(kv_scale is not None, "kv_scale: required for an FP8 cache")
+        need(kv_scale.dtype == torch.float32 and tuple(kv_scale.shape) == (p.num_pages, PAGE_SIZE),
+             f"kv_scale: expected float32 [{p.num_pages}, {PAGE_SIZE}], got {kv_scale.dtype} {tuple(kv_scale.shape)}")
+        on_dev(kv_scale, "kv_scale")
+    else:
+        need(tuple(kv_cache.shape) == kv_shape and kv_cache.element_size() == 2,
+             f"kv_cache: expected 16-bit bf16 values of shape {kv_shape}, got {kv_cache.dtype} {tuple(kv_cache.shape)}")
+        need(kv_scale is None, "kv_scale: only an FP8 cache takes scales")
+    on_dev(kv_cache, "kv_cache")
+    need(block_table.dtype == torch.int32 and tuple(block_table.shape) == (B, p.max_blocks_per_seq),
+         f"block_table: expected int32 [{B}, {p.max_blocks_per_seq}], got {block_table.dtype} {tuple(block_table.shape)}")
+    on_dev(block_table, "block_table")
+    need(seqlens.dtype == torch.int32 and tuple(seqlens.shape) == (B,),
+         f"seqlens: expected int32 [{B}], got {seqlens.dtype} {tuple(seqlens.shape)}")
+    on_dev(seqlens, "seqlens")
+
+
 class MlaDecode:
     """One decode configuration bound to torch tensors on the current HIP device.
 
@@ -293,7 +351,7 @@ class MlaDecode:
         self.params = make_params(batch=batch, seqlen_q=seqlen_q, num_heads=num_heads, num_pages=num_pages,
                                   max_blocks_per_seq=max_blocks_per_seq, kv_dtype=kv_dtype, causal=causal,
                                   softmax_scale=softmax_scale, num_workgroups=num_workgroups)
-        self.device = torch.device(device)
+        self.device = _resolve_device(device)
         self.workspace_bytes = mla_get_workspace(self.params)
         # 256-byte aligned: the caching allocator hands out 512-byte aligned blocks.
         self.workspace = torch.empty(self.workspace_bytes, dtype=torch.uint8, device=self.device)
@@ -304,10 +362,15 @@ class MlaDecode:
         return self.torch.cuda.current_stream(self.device).cuda_stream
 
     def plan(self, seqlens) -> None:
+        import torch
+        if seqlens.dtype != torch.int32 or tuple(seqlens.shape) != (self.params.batch,) or \
+                seqlens.device != self.device or not seqlens.is_contiguous():
+            raise ValueError(f"seqlens: expected a contiguous int32 [{self.params.batch}] tensor on {self.device}")
         mla_get_workspace(self.params, seqlens.data_ptr(), self.workspace.data_ptr(), self.workspace_bytes,
                           self._stream())
 
     def decode(self, q, kv_cache, block_table, seqlens, kv_scale=None) -> None:
+        check_decode_inputs(self.params, self.device, q, kv_cache, block_table, seqlens, kv_scale)
         mla_decode_fwd(self.params, q.data_ptr(), kv_cache.data_ptr(), 0 if kv_scale is None else kv_scale.data_ptr(),
                        block_table.data_ptr(), seqlens.data_ptr(), self.workspace.data_ptr(), self.workspace_bytes,
                        self.out.data_ptr(), self.lse.data_ptr(), self._stream())

@@ -205,8 +205,8 @@ int mla_splitkv_combine(const mla_decode_params* p, const void* workspace, size_
   const int rows = p->seqlen_q * p->num_heads;
   const Layout lay = make_layout(p->batch, rows, nwg);
   if (workspace_bytes < lay.total) return MLA_ERR_WORKSPACE_TOO_SMALL;
-  if (launch_combine(static_cast<const char*>(workspace), lay, p->batch, rows, static_cast<uint16_t*>(out), lse,
-                     (hipStream_t)stream) != hipSuccess)
+  if (launch_combine(static_cast<const char*>(workspace), lay, p->batch, rows, nwg, p->max_blocks_per_seq,
+                     static_cast<uint16_t*>(out), lse, (hipStream_t)stream) != hipSuccess)
     return MLA_ERR_HIP;
   return MLA_OK;
 }
@@ -241,7 +241,7 @@ int mla_workspace_flags(const void* workspace, uint32_t* flags, void* stream) {
   if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return MLA_ERR_HIP;
   Header h;
   if (hipMemcpy(&h, workspace, sizeof h, hipMemcpyDeviceToHost) != hipSuccess) return MLA_ERR_HIP;
-  *flags = h.magic == kMagic ? h.flags : 0u;
+  *flags = h.magic == kMagic ? h.flags : (uint32_t)MLA_FLAG_BAD_PLAN;   // never planned
   return MLA_OK;
 }
 

@@ -39,12 +39,23 @@ constexpr int kThreadsPerRow = kHeadDimV / kCols;       // 64
 constexpr int kRowsPerWg = kThreads / kThreadsPerRow;   // 4
 constexpr int kGroup = 4;                               // pieces loaded together
 
-__global__ __launch_bounds__(kThreads) void mla_combine_kernel(const char* __restrict__ ws, Layout lay, int rows,
+__global__ __launch_bounds__(kThreads) void mla_combine_kernel(const char* __restrict__ ws, Layout lay, int batch,
+                                                               int rows, int nwg, int max_blocks,
                                                                uint16_t* __restrict__ out, float* __restrict__ lse) {
   const int b = blockIdx.x;
   const int row = blockIdx.y * kRowsPerWg + threadIdx.x / kThreadsPerRow;
   const int col = (threadIdx.x % kThreadsPerRow) * kCols;
   if (row >= rows) return;
+  // A plan made for other parameters (or none): the decode has written the empty
+  // result and flagged it; nothing here may be trusted.
+  {
+    Header h;
+    const int32_t CONST_AS* src = (const int32_t CONST_AS*)(ws + lay.header);
+    int32_t* dst = reinterpret_cast<int32_t*>(&h);
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(Header) / 4); i++) dst[i] = src[i];
+    if (!header_matches(h, batch, rows, nwg, max_blocks)) return;
+  }
   // Request info is uniform over the workgroup: scalar loads.
   const int32_t CONST_AS* rqp = (const int32_t CONST_AS*)(ws + lay.req_info + sizeof(ReqInfo) * b);
   const int npages = rqp[offsetof(ReqInfo, npages) / 4], nsplit = rqp[offsetof(ReqInfo, nsplit) / 4],
@@ -121,9 +132,10 @@ __global__ __launch_bounds__(kThreads) void mla_combine_kernel(const char* __res
 
 }  // namespace
 
-hipError_t launch_combine(const char* ws, const Layout& lay, int batch, int rows, uint16_t* out, float* lse,
-                          hipStream_t stream) {
-  void* args[] = {(void*)&ws, (void*)&lay, (void*)&rows, (void*)&out, (void*)&lse};
+hipError_t launch_combine(const char* ws, const Layout& lay, int batch, int rows, int nwg, int max_blocks,
+                          uint16_t* out, float* lse, hipStream_t stream) {
+  void* args[] = {(void*)&ws, (void*)&lay, (void*)&batch, (void*)&rows, (void*)&nwg, (void*)&max_blocks,
+                  (void*)&out, (void*)&lse};
   const dim3 grid(batch, (rows + kRowsPerWg - 1) / kRowsPerWg);
   return hipLaunchKernel((const void*)mla_combine_kernel, grid, dim3(kThreads), args, 0, stream);
 }

@@ -45,6 +45,7 @@
 #include <hip/hip_runtime.h>
 
 #define MLA_HD __host__ __device__
+#include "mla_decode.h"
 #include "mla_launch.h"
 #include "mla_workspace.h"
 
@@ -232,6 +233,23 @@ __device__ __forceinline__ i16x4_t lds_read_tr16(const char LDS_AS* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<i16x4_t LDS_AS*>(const_cast<char LDS_AS*>(p)));
 }
 
+// The plan in the workspace does not belong to this call: every workgroup writes
+// the defined empty result (out = 0, lse = -inf) for its share of the rows --
+// requests stretch, stretch + nwg, ... and row block rb -- and nothing else is
+// read.  8-byte stores: out is only required to be 8-byte aligned.
+__device__ __forceinline__ void write_empty_rows(const DecodeArgs& a, int stretch, int rb) {
+  Header* hdr = reinterpret_cast<Header*>(a.ws + a.lay.header);
+  if (threadIdx.x == 0 && stretch == 0 && rb == 0) atomicOr(&hdr->flags, (uint32_t)MLA_FLAG_BAD_PLAN);
+  const int r0 = rb * kRowsPerBlock;
+  const int nr = a.rows - r0 < kRowsPerBlock ? a.rows - r0 : kRowsPerBlock;
+  constexpr int kPieces = kHeadDimV / 4;   // 8-byte pieces per row
+  for (int b = stretch; b < a.batch; b += a.nwg) {
+    uint2* orow = reinterpret_cast<uint2*>(a.out + ((size_t)b * a.rows + r0) * kHeadDimV);
+    for (int g = threadIdx.x; g < nr * kPieces; g += blockDim.x) orow[g] = make_uint2(0u, 0u);
+    for (int r = threadIdx.x; r < nr; r += blockDim.x) a.lse[(size_t)b * a.rows + r0 + r] = -INFINITY;
+  }
+}
+
 __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem_raw[kSlots * kSlotBytes];
   char LDS_AS* smem = (char LDS_AS*)(smem_raw);
@@ -253,8 +271,13 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
   const int rb = lin - stretch * a.nrb;
 
   Header* hdr = reinterpret_cast<Header*>(a.ws + a.lay.header);
+  const Header plan_hdr = load_const<Header>(a.ws + a.lay.header);
   const WgInfo wg = load_const<WgInfo>(a.ws + a.lay.wg_info + sizeof(WgInfo) * stretch);
   const char* reqs = a.ws + a.lay.req_info;
+  if (!header_matches(plan_hdr, a.batch, a.rows, a.nwg, a.max_blocks)) {
+    write_empty_rows(a, stretch, rb);
+    return;
+  }
   if (wg.page_begin >= wg.page_end) return;
 
   const int row_local = wave * kRowsPerWave + n;
@@ -487,7 +510,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
         }
       } else {
         const int slot_id = rq.slot_off + split;
-        if (slot_id < 2 * a.nwg) {
+        if (slot_id >= 0 && slot_id < 2 * a.nwg) {
           const size_t pidx = ((size_t)slot_id * a.nrb + rb) * kRowsPerBlock + orow_local;
           store_partial(a, pidx, oq, o, inv, lse_v);
         }
@@ -582,8 +605,13 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_fp8_kernel(DecodeArgs 
   const int rb = lin - stretch * a.nrb;
 
   Header* hdr = reinterpret_cast<Header*>(a.ws + a.lay.header);
+  const Header plan_hdr = load_const<Header>(a.ws + a.lay.header);
   const WgInfo wg = load_const<WgInfo>(a.ws + a.lay.wg_info + sizeof(WgInfo) * stretch);
   const char* reqs = a.ws + a.lay.req_info;
+  if (!header_matches(plan_hdr, a.batch, a.rows, a.nwg, a.max_blocks)) {
+    write_empty_rows(a, stretch, rb);
+    return;
+  }
   if (wg.page_begin >= wg.page_end) return;
 
   const int row_local = wave * kRowsPerWave + n;
@@ -857,7 +885,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_fp8_kernel(DecodeArgs 
         }
       } else {
         const int slot_id = rq.slot_off + split;
-        if (slot_id < 2 * a.nwg) {
+        if (slot_id >= 0 && slot_id < 2 * a.nwg) {
           const size_t pidx = ((size_t)slot_id * a.nrb + rb) * kRowsPerBlock + orow_local;
           store_partial(a, pidx, oq, o, inv, lse_v);
         }

@@ -259,7 +259,9 @@ __global__ __launch_bounds__(kPlanThreads) void mla_plan_kernel(const int32_t* _
     h.max_slots = 2 * nwg;
     h.total_pages = total_pages;
     h.used_slots = carry;
-    for (int i = 0; i < 7; i++) h.pad[i] = 0;
+    h.max_blocks = max_blocks;
+    h.seqlen_q = seqlen_q;
+    for (int i = 0; i < 5; i++) h.pad[i] = 0;
     *hdr = h;
   }
 }

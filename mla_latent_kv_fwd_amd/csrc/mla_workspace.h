@@ -22,6 +22,8 @@ constexpr int kMaxStretches = 4096;  // persistent workgroups per row block
 constexpr int kPlanCostPerRequest = 3;  // fixed cost of a request segment (set-up + finalise), in pages
 constexpr uint32_t kMagic = 0x4D4C4131u;  // "MLA1"
 
+MLA_HD inline int row_blocks(int rows) { return (rows + kRowsPerBlock - 1) / kRowsPerBlock; }
+
 // Per persistent workgroup (stretch) of the plan.
 struct WgInfo {
   int32_t page_begin;  // first page (global position in the concatenation of all requests' pages)
@@ -54,8 +56,17 @@ struct Header {
   int32_t max_slots;    // partial slots reserved (2 * nwg)
   int32_t total_pages;
   int32_t used_slots;
-  int32_t pad[7];
+  int32_t max_blocks;   // row stride of the block table the plan clamped lengths to
+  int32_t seqlen_q;
+  int32_t pad[5];
 };
+
+// The decode and combine kernels trust the plan only when the header matches
+// their own parameters (one scalar load of the header per workgroup).
+MLA_HD inline bool header_matches(const Header& h, int batch, int rows, int nwg, int max_blocks) {
+  return h.magic == kMagic && h.batch == batch && h.rows == rows && h.nwg == nwg && h.nrb == row_blocks(rows) &&
+         h.max_slots == 2 * nwg && h.max_blocks == max_blocks;
+}
 
 // Byte offsets of every region; all 256-byte aligned.  A split request's piece
 // is stored per row as an LSE, a power-of-two scale s and the normalised output
@@ -66,7 +77,6 @@ struct Layout {
 
 MLA_HD inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-MLA_HD inline int row_blocks(int rows) { return (rows + kRowsPerBlock - 1) / kRowsPerBlock; }
 
 MLA_HD inline Layout make_layout(int batch, int rows, int nwg) {
   Layout l;
