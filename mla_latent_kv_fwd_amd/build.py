@@ -52,6 +52,44 @@ def build(isa_dir: str | None = None) -> str:
     return LIB
 
 
+# Host-side sanitizers for the C ABI code (argument checks, sizing, launch set-up).  Each -fsanitize flag goes
+# to the host compilation only; the device code is built as usual.
+HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+
+
+def build_host_sanitized(out_dir: str) -> str:
+    """libmla_decode.so with the C ABI source (mla_api.hip) built with AddressSanitizer and
+    UndefinedBehaviorSanitizer on its host code, linked with the other sources' usual objects.  The process
+    that loads it must preload the compiler's ASan runtime (tests/test_sanitizers.py does)."""
+    os.makedirs(out_dir, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    objs = []
+    for src in srcs:
+        obj = os.path.join(out_dir, os.path.basename(src)[:-4] + ".o")
+        if os.path.basename(src) == "mla_api.hip":
+            cmd = [HIPCC, *FLAGS, *HOST_SANITIZE, "-c", src, "-o", obj]
+            r = subprocess.run(cmd, capture_output=True, text=True)
+            if r.returncode != 0:
+                raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
+        else:
+            _compile(src, obj, None)
+        objs.append(obj)
+    lib = os.path.join(out_dir, "libmla_decode.so")
+    subprocess.check_call([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", lib, *objs])
+    return lib
+
+
+def asan_runtime() -> str:
+    """The clang ASan runtime that matches hipcc's host compiler."""
+    r = subprocess.run([HIPCC, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = r.stdout.strip()
+    if not os.path.isabs(path) or not os.path.exists(path):
+        cands = glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so")
+        path = cands[0] if cands else ""
+    return path
+
+
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--isa", default=None, help="directory to keep intermediate files (assembly) in")

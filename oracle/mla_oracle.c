@@ -31,7 +31,8 @@
  *    paragraph: paged KV with block size 64; FlashMLA guide, Architecture 1).
  *  - With several new tokens per request, seqlen counts the new tokens and new
  *    token i sees the keys up to and including itself: L - s_q + 1 + i keys
- *    (handbook page, FLOP script: "k includes the new tokens", causal pairs).
+ *    (handbook page, FLOP script: its cached-token count already holds the
+ *    new tokens, and its causal pair count is the sum of these key counts).
  *  - FP8 cache: OCP E4M3FN codes (1 sign, 4 exponent, 3 mantissa bits, max 448;
  *    "MLA and FP8 MoE Serving", section on FP8 formats) times a per-token fp32
  *    scale.

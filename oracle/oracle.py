@@ -28,7 +28,11 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "mla_oracle.c")
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# ORACLE_SANITIZE=1 selects a build with AddressSanitizer and UndefinedBehaviorSanitizer (gcc's runtimes must then
+# be preloaded into the process; tests/test_sanitizers.py does that in a child process).
+_SANITIZE = os.environ.get("ORACLE_SANITIZE") == "1"
+_LIB_PATH = os.path.join(_HERE, "liboracle_asan.so" if _SANITIZE else "liboracle.so")
+_SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g"]
 
 Q_BF16, Q_F64 = 0, 1
 KV_BF16, KV_E4M3FN = 0, 1
@@ -47,7 +51,7 @@ def build(force: bool = False) -> str:
     if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
         tmp = _LIB_PATH + ".tmp"
         subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
-                               "-o", tmp, _SRC, "-lm"])
+                               *(_SAN_FLAGS if _SANITIZE else []), "-o", tmp, _SRC, "-lm"])
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
 
