@@ -1,26 +1,31 @@
 #!/usr/bin/env python3
 """Benchmark of one MLA absorb-path decode step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--copies C] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--copies C] [--no-cpu] [--no-configs]
 
-A step is the whole hot path over one batch of synthetic inputs already
-resident in HBM: the split plan, the attention kernel over the paged cache and
-the LSE combine.  The timed region holds exactly K steps between device
+A step is one decode of one layer over one batch of synthetic inputs already
+resident in HBM: the attention kernel over the paged cache and the LSE combine
+of the split requests.  The split plan is computed once per model step from the
+sequence lengths and serves every layer, so it runs once before the timed
+region and is timed on its own (``kernel_ms.plan``; ``ms_per_step_with_plan``
+adds it to the step).  The timed region holds exactly K steps between device
 synchronisations.  The cache is cycled over C independent copies so repeats
 cannot be served from the 256 MB last-level cache (C is chosen so the copies
-total at least twice that, unless given).
+total at least twice that, unless given); ``warm_single_copy`` repeats the
+step on one copy, labelled as such.
 
-Prints one JSON line.  ``value`` is algorithmic TFLOP/s of the whole step;
-``projections`` times the two per-head projections on either side of the step
-(W_UK absorbed into the query, W_UV on the latent output) separately, and
-``prefill`` the chunked expand path on 512 new tokens after a 32K prefix (or,
-with ``--prefill prefill_h128_n8192``, a prefill of 8K new tokens);
-``roofline`` describes the attention kernel alone (its launches are timed with
-HIP events on the stream it runs on, inside the timed region, on every 10th
-step; the plan and combine are timed in a separate pass because each event pair
-costs GPU time); ``cpu_baseline`` is the fp64 oracle run on a bounded sample of
-the same workload's rows on the host cores.  Every timed leg starts after the
-GPU has been kept busy for a while, so that its clocks have left the idle state.
+Prints one JSON line.  ``value`` is algorithmic TFLOP/s of the step on the
+headline workload (or --config); ``roofline`` describes the attention kernel
+alone: its average duration over at least 100 back-to-back launches between
+one HIP event pair on the stream it runs on; ``parity`` compares the step's
+output with the fp64 oracle on the rows of ``cpu_baseline``'s sample;
+``configs`` repeats the measurement on the other measured workloads (ragged
+batch, two new tokens, FP8 cache) with parity on sampled rows; ``projections``
+times the two per-head projections on either side of the step and ``prefill``
+the chunked expand path on 512 new tokens after a 32K prefix.  Step times are
+reported as the mean over the timed region and as p10 / p50 / p90 of blocks of
+10 steps.  Every timed leg starts after the GPU has been kept busy for a
+while, so that its clocks have left the idle state.
 """
 from __future__ import annotations
 
@@ -38,45 +43,60 @@ D_LATENT, D_ROPE, D_NOPE, D_V = 512, 64, 128, 128
 
 
 # ---------------------------------------------------------------- algorithmic accounting
-def pair_flops_absorb(H, dc=D_LATENT, dr=D_ROPE):
-    """FLOPs per (query token, cached token) pair on the absorb path: a (dc+dr)-wide score and a
-    dc-wide weighted sum for each of H heads (handbook FLOP script)."""
-    return 2 * H * (dc + dr) + 2 * H * dc
+# Counted from the contractions the kernels perform.  For one visible cached token and all H heads of one new
+# token, the absorb path forms a D_QK-wide score per head (QK^T) and adds a D_LATENT-wide weighted row per head (PV),
+# a multiply-add counting 2 FLOPs.  tests/test_bench_accounting.py checks these counts against the figures the
+# handbook prints ("MLA inference: two computation paths and FlashMLA", section "Which is faster: count new tokens
+# and cached tokens").
+D_QK = D_LATENT + D_ROPE
 
 
-def pair_flops_expand(H, dn=D_NOPE, dr=D_ROPE, dv=D_V):
-    return 2 * H * (dn + dr) + 2 * H * dv
+def visible_keys(L, s_q, causal):
+    """Cached tokens each of the s_q new-token rows of a request attends to.  L counts the new tokens themselves;
+    with the causal mask, new token i (0-based) sees every earlier token and itself: L - s_q + 1 + i keys."""
+    return [L - s_q + 1 + i if causal else L for i in range(s_q)]
 
 
-def expand_flops_per_cached_token(H, dc=D_LATENT, dn=D_NOPE, dv=D_V):
-    return 2 * dc * H * (dn + dv)
+def decode_flops_per_key(H):
+    """One visible key for the H heads of one new token: a D_QK-wide dot product (score) and a D_LATENT-wide
+    weighted row (value) per head."""
+    return H * (2 * D_QK + 2 * D_LATENT)
 
 
-def absorb_flops_per_new_token(H, dc=D_LATENT, dn=D_NOPE, dv=D_V):
-    return 2 * H * dn * dc + 2 * H * dc * dv
-
-
-def causal_pairs(q, k):
-    """(query, key) pairs when q new tokens follow and are counted in k tokens, causal among the new ones."""
-    return q * k - q * (q - 1) // 2
-
-
-def kv_bytes_per_token(dtype="bf16", dc=D_LATENT, dr=D_ROPE):
-    """Cache bytes read per cached token: 2 bytes per number in bf16; 1 per number plus a 4-byte scale in FP8."""
-    return (dc + dr) * 2 if dtype == "bf16" else (dc + dr) + 4
+def kv_bytes_per_token(kv_dtype="bf16"):
+    """Bytes of one cached token: its D_QK stored numbers (2 bytes each in bf16; 1 byte each in E4M3FN, plus the
+    token's fp32 scale)."""
+    return D_QK * 2 if kv_dtype == "bf16" else D_QK + 4
 
 
 def workload_counts(seqlens, H, s_q, causal, kv_dtype="bf16"):
-    """(FLOPs, KV bytes, total algorithmic bytes) of one decode step over these requests."""
-    pairs = 0
-    for L in seqlens:
-        pairs += causal_pairs(s_q, int(L)) if causal else s_q * int(L)
-    flops = pairs * pair_flops_absorb(H)
+    """(FLOPs, KV bytes, total algorithmic bytes) of one decode step over these requests.  The total adds q~ read
+    once, the bf16 output and fp32 LSE written once, and the block-table entries and lengths read."""
+    keys = sum(sum(visible_keys(int(L), s_q, causal)) for L in seqlens)
+    flops = keys * decode_flops_per_key(H)
     kv = sum(int(L) for L in seqlens) * kv_bytes_per_token(kv_dtype)
     B = len(seqlens)
-    io = B * s_q * H * (D_LATENT + D_ROPE) * 2 + B * s_q * H * D_LATENT * 2 + B * s_q * H * 4
+    io = B * s_q * H * (D_QK * 2 + D_LATENT * 2 + 4)
     tables = B * 4 + sum(-(-int(L) // 64) for L in seqlens) * 4
     return flops, kv, kv + io + tables
+
+
+def expansion_flops_per_token(H):
+    """The expand path's per-head products of one cached latent: W_UK[h] (D_NOPE x D_LATENT) and W_UV[h]
+    (D_V x D_LATENT) applied to the D_LATENT-wide latent."""
+    return H * 2 * D_LATENT * (D_NOPE + D_V)
+
+
+def mha_flops_per_key(H):
+    """One (query, key) pair of the expand path's attention: a (D_NOPE + D_ROPE)-wide score and a D_V-wide
+    weighted row per head."""
+    return H * (2 * (D_NOPE + D_ROPE) + 2 * D_V)
+
+
+def projection_flops_per_token(H):
+    """The absorb path's two per-head projections of one new token: q^N (D_NOPE) through W_UK[h]^T to the
+    D_LATENT-wide absorbed query, and the D_LATENT-wide latent output through W_UV[h] to D_V."""
+    return H * 2 * D_LATENT * (D_NOPE + D_V)
 
 
 # ---------------------------------------------------------------- benchmark
@@ -87,12 +107,15 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default=None)
     ap.add_argument("--copies", type=int, default=0, help="independent cache copies to cycle (0 = auto)")
-    ap.add_argument("--event-every", type=int, default=10,
-                    help="record the attention kernel's event pair on every Nth timed step")
+    ap.add_argument("--block", type=int, default=10, help="steps per event-timed block (percentiles)")
+    ap.add_argument("--roofline-launches", type=int, default=200,
+                    help="back-to-back attention launches timed for the roofline (at least 100)")
     ap.add_argument("--warm-seconds", type=float, default=WARM_SECONDS,
                     help="keep the GPU busy this long after the W warm-up steps (0 for counter runs)")
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline and the parity check")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target duration of the CPU baseline sample")
+    ap.add_argument("--no-configs", action="store_true", help="measure only the main workload")
+    ap.add_argument("--config-steps", type=int, default=200, help="timed steps for each of the other workloads")
     ap.add_argument("--no-proj", action="store_true", help="skip the projection kernels' measurement")
     ap.add_argument("--no-prefill", action="store_true", help="skip the expand-path (prefill) measurement")
     ap.add_argument("--prefill", default="extend_h128_p32768_n512", choices=sorted(PREFILL_WORKLOADS),
@@ -224,10 +247,9 @@ PREFILL_WORKLOADS = {
 
 
 def prefill_counts(H, n, L):
-    """Algorithmic FLOPs of the expand path for n new tokens after L - n cached ones: expanding every one of
-    the L cached tokens into K and V for H heads, plus the causal (query, key) pairs at 2H(192 + 128) each
-    (the handbook's path-one accounting)."""
-    return L * expand_flops_per_cached_token(H) + causal_pairs(n, L) * pair_flops_expand(H)
+    """Algorithmic FLOPs of the expand path for n new tokens after L - n cached ones: the expansion of each of the
+    L cached latents into per-head keys and values, plus the attention over every visible (query, key) pair."""
+    return L * expansion_flops_per_token(H) + sum(visible_keys(L, n, True)) * mha_flops_per_key(H)
 
 
 def bench_prefill(torch, M, W, name, launches=10):
@@ -258,145 +280,239 @@ def bench_prefill(torch, M, W, name, launches=10):
                       "not part of the step"}
 
 
+def oracle_rows(wl, rows):
+    """fp64 oracle output and LSE of the given flat (request, new token, head) rows, and the seconds it took."""
+    from oracle import oracle as O
+    t0 = time.perf_counter()
+    o, l = O.attend(wl.q, wl.cache, wl.block_table, wl.seqlens, softmax_scale=wl.softmax_scale, causal=wl.causal,
+                    kv_scale=wl.kv_scale, rows=rows)
+    return o, l, time.perf_counter() - t0
+
+
+def rows_flops(wl, rows):
+    H, s_q = wl.num_heads, wl.s_q
+    return sum(visible_keys(int(wl.seqlens[int(r) // (s_q * H)]), s_q, wl.causal)[(int(r) // H) % s_q] *
+               decode_flops_per_key(1) for r in rows)
+
+
 def cpu_baseline(wl, target_s):
-    """fp64 oracle on a bounded sample of rows; returns the dict for the JSON line."""
+    """fp64 oracle on a bounded sample of rows, sized to take about target_s seconds on the host's cores.
+    Returns the dict for the JSON line and (rows, out, lse) for the parity check."""
     import numpy as np
     from oracle import oracle as O
     total = wl.batch * wl.s_q * wl.num_heads
     rng = np.random.default_rng(0)
-
-    def run(n):
-        rows = np.sort(rng.choice(total, size=min(n, total), replace=False)).astype(np.int64)
-        t0 = time.perf_counter()
-        O.attend(wl.q, wl.cache, wl.block_table, wl.seqlens, softmax_scale=wl.softmax_scale, causal=wl.causal,
-                 kv_scale=wl.kv_scale, rows=rows)
-        dt = time.perf_counter() - t0
-        H, s_q = wl.num_heads, wl.s_q
-        flops = 0
-        for r in rows:
-            b, i = int(r) // (s_q * H), (int(r) // H) % s_q
-            L = int(wl.seqlens[b])
-            n = (L - s_q + 1 + i) if wl.causal else L
-            flops += n * pair_flops_absorb(1)
-        return len(rows), dt, flops
-
-    n0, dt0, _ = run(max(8, O.num_threads()))
-    n = int(min(total, max(n0, n0 * target_s / max(dt0, 1e-3))))
-    n, dt, flops = run(n)
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": O.num_threads(), "kind": "oracle",
-            "sample": f"{n} of {total} query rows (fp64, {dt:.1f} s)"}
+    pick = lambda n: np.sort(rng.choice(total, size=min(n, total), replace=False)).astype(np.int64)
+    rows = pick(max(8, O.num_threads()))
+    _, _, dt0 = oracle_rows(wl, rows)
+    n = int(min(total, max(len(rows), len(rows) * target_s / max(dt0, 1e-3))))
+    rows = pick(n)
+    o, l, dt = oracle_rows(wl, rows)
+    res = {"value": round(rows_flops(wl, rows) / dt / 1e12, 6), "unit": "TFLOP/s", "cores": O.num_threads(),
+           "kind": "oracle", "sample": f"{len(rows)} of {total} query rows of {wl.name} (fp64, {dt:.1f} s)"}
+    return res, (rows, o, l)
 
 
-def main():
-    args = _parse()
-    if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1"}))
-        return 2
-    if args.copy_probe:
-        return copy_probe()
+def parity(M, W, out, lse, rows, ref_o, ref_l, bf16_tol=True):
+    """Output and LSE of the GPU step on these rows against the oracle's (the tests' tolerances)."""
     import numpy as np
-    import torch
-    import workloads as W
-    import mla_latent_kv_fwd_amd as M
+    got = W.bf16_bits_to_f32(out.reshape(-1, M.HEAD_DIM_V)[rows]).astype(np.float64)
+    gl = lse.reshape(-1)[rows].astype(np.float64)
+    d = got - ref_o
+    per_row = np.linalg.norm(d, axis=1) / np.maximum(np.linalg.norm(ref_o, axis=1), 1e-30)
+    rel = float(np.linalg.norm(d) / max(np.linalg.norm(ref_o), 1e-30))
+    mx = float(np.abs(d).max())
+    lerr = float(np.abs(gl - ref_l).max())
+    ok = rel <= 5e-3 and mx <= 2e-2 and lerr <= 1e-3 if bf16_tol else rel <= 3e-2
+    return {"rows": int(len(rows)), "of": int(out.reshape(-1, M.HEAD_DIM_V).shape[0]), "out_max_abs": mx,
+            "out_rel_l2": rel, "worst_row_rel_l2": float(per_row.max()), "worst_row": int(rows[int(per_row.argmax())]),
+            "lse_max_abs": lerr, "within_tolerance": bool(ok)}
 
-    name = args.config or W.HEADLINE
+
+def percentiles(xs):
+    import numpy as np
+    a = np.asarray(xs, dtype=np.float64)
+    return {"p10": round(float(np.percentile(a, 10)), 5), "p50": round(float(np.percentile(a, 50)), 5),
+            "p90": round(float(np.percentile(a, 90)), 5)}
+
+
+def roofline_of(flops, alg_bytes, kernel_ms, traffic):
+    """Binding roofline of the attention kernel: whichever of HBM bytes and bf16 MFMA time is larger."""
+    gbps = alg_bytes / (kernel_ms * 1e-3) / 1e9
+    tfl = flops / (kernel_ms * 1e-3) / 1e12
+    if flops / (BF16_MFMA_PEAK_TFLOPS * 1e12) > alg_bytes / (HBM_PEAK_GBPS * 1e9):
+        return {"bound": "mfma", "achieved": round(tfl, 2), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tfl / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": traffic}
+    return {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic}
+
+
+def measure(torch, M, W, name, *, steps, warmup, warm_seconds, copies=0, block=10, roof_launches=200,
+            parity_rows=None, plan_launches=50):
+    """Time one workload: plan once; W warm-up steps and warm_seconds of untimed ones; exactly `steps` timed steps
+    (decode + combine) between synchronisations; then the attention kernel alone for the roofline, the plan alone,
+    the combine alone, and the step on a single cache copy.  Returns (dict, workload, out, lse)."""
+    import numpy as np
     wl = W.make_config(name)
     dev = torch.device("cuda")
     kv_np = wl.cache.view(np.int16) if wl.cache.dtype == np.uint16 else wl.cache
     kv_bytes_total = wl.cache.nbytes + (0 if wl.kv_scale is None else wl.kv_scale.nbytes)
-    copies = args.copies or max(1, math.ceil(2 * MALL_BYTES / kv_bytes_total))
+    copies = copies or max(1, math.ceil(2 * MALL_BYTES / kv_bytes_total))
     kvs = [torch.from_numpy(kv_np).to(dev) for _ in range(copies)]
     kss = [None if wl.kv_scale is None else torch.from_numpy(wl.kv_scale).to(dev) for _ in range(copies)]
     q = torch.from_numpy(wl.q.view(np.int16)).to(dev)
     bt = torch.from_numpy(wl.block_table).to(dev)
     sl = torch.from_numpy(wl.seqlens).to(dev)
+    fp8 = wl.kv_dtype == "fp8_e4m3fn"
     dec = M.MlaDecode(batch=wl.batch, seqlen_q=wl.s_q, num_heads=wl.num_heads, num_pages=wl.num_pages,
                       max_blocks_per_seq=wl.block_table.shape[1], causal=wl.causal,
-                      kv_dtype=M.MLA_KV_FP8_E4M3FN if wl.kv_dtype == "fp8_e4m3fn" else M.MLA_KV_BF16,
-                      softmax_scale=float(wl.softmax_scale))
+                      kv_dtype=M.MLA_KV_FP8_E4M3FN if fp8 else M.MLA_KV_BF16, softmax_scale=float(wl.softmax_scale))
     stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    dec.plan(sl)   # once: the plan depends only on the lengths and serves every step
 
-    # Event pairs cost GPU time on this stack (each recorded pair adds several us to
-    # the step it sits in), so inside the timed region only the attention kernel --
-    # the one the roofline describes -- is bracketed, and only on every
-    # --event-every'th step; the plan and combine are timed in a separate pass.
-    def step(i, ev=None, all_kernels=False):
-        if ev is not None and all_kernels:
-            ev[0].record(stream)
-        dec.plan(sl)
-        if ev is not None:
-            ev[1].record(stream)
-        dec.decode(q, kvs[i % copies], bt, sl, kss[i % copies])
-        if ev is not None:
-            ev[2].record(stream)
+    def step(i, c=None):
+        k = i % copies if c is None else c
+        dec.decode(q, kvs[k], bt, sl, kss[k])
         dec.combine()
-        if ev is not None and all_kernels:
-            ev[3].record(stream)
 
-    every = max(1, args.event_every)
-    evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(4)] for i in range(0, args.steps, every)}
-    # Warm-up: the W steps asked for, then untimed steps until the GPU has been busy
-    # for WARM_SECONDS (clock ramp), ending right before the timed region.
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
-    warm_total = args.warmup + keep_busy(torch, lambda i: step(i), seconds=args.warm_seconds, min_calls=0)
+    warm_total = warmup + keep_busy(torch, step, seconds=warm_seconds, min_calls=0)
 
-    # Timed region: exactly `steps` steps, synchronised on both sides.
+    # Timed region: exactly `steps` steps, synchronised on both sides; an event at every block boundary.
+    nblk = max(1, steps // block)
+    marks = [ev() for _ in range(nblk + 1)]
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i, evs.get(i))
+    for i in range(steps):
+        if i % block == 0 and i // block <= nblk:
+            marks[i // block].record(stream)
+        step(i)
+    if steps % block == 0:
+        marks[nblk].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    dec_ms = [e[1].elapsed_time(e[2]) for e in evs.values()]
+    blocks = [marks[j].elapsed_time(marks[j + 1]) / block for j in range(nblk) if (j + 1) * block <= steps]
+    ms_per_step = wall * 1e3 / steps
+    out_np = dec.out.view(torch.int16).cpu().numpy().view(np.uint16)
+    lse_np = dec.lse.cpu().numpy()
+    flags = dec.flags()
 
-    # Per-kernel breakdown (outside the timed region): events around every kernel.
-    nb = min(args.steps, 50)
-    evb = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(nb)]
-    for i in range(nb):
-        step(i, evb[i], all_kernels=True)
+    # The attention kernel alone: back-to-back launches between one event pair (roofline).
+    R = max(100, roof_launches)
+    keep_busy(torch, step, seconds=0.05, min_calls=0)
+    e0, e1 = ev(), ev()
+    e0.record(stream)
+    for i in range(R):
+        dec.decode(q, kvs[i % copies], bt, sl, kss[i % copies])
+    e1.record(stream)
     torch.cuda.synchronize()
-    plan_ms = [e[0].elapsed_time(e[1]) for e in evb]
-    comb_ms = [e[2].elapsed_time(e[3]) for e in evb]
-    ms_per_step = wall * 1e3 / args.steps
+    dec_ms = e0.elapsed_time(e1) / R
+    # The plan alone and the combine alone (back-to-back launches; the combine re-merges the same pieces).
+    e0, e1 = ev(), ev()
+    e0.record(stream)
+    for _ in range(plan_launches):
+        dec.plan(sl)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    plan_ms = e0.elapsed_time(e1) / plan_launches
+    e0, e1 = ev(), ev()
+    e0.record(stream)
+    for _ in range(plan_launches):
+        dec.combine()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    comb_ms = e0.elapsed_time(e1) / plan_launches
+    # The step on one cache copy (partly served by the last-level cache: labelled, not the headline).
+    keep_busy(torch, lambda i: step(i, 0), seconds=0.05, min_calls=0)
+    e0, e1 = ev(), ev()
+    e0.record(stream)
+    for i in range(steps):
+        step(i, 0)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    warm1_ms = e0.elapsed_time(e1) / steps
+
     flops, kv_bytes, alg_bytes = workload_counts(wl.seqlens, wl.num_heads, wl.s_q, wl.causal, wl.kv_dtype)
-    dec_avg = float(np.mean(dec_ms))
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     kv_gbps = kv_bytes / (ms_per_step * 1e-3) / 1e9
-    dec_gbps = alg_bytes / (dec_avg * 1e-3) / 1e9
-    dec_tflops = flops / (dec_avg * 1e-3) / 1e12
-    mfma_bound = flops / (BF16_MFMA_PEAK_TFLOPS * 1e12) > alg_bytes / (HBM_PEAK_GBPS * 1e9)
-    if mfma_bound:
-        roof = {"bound": "mfma", "achieved": round(dec_tflops, 2), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(dec_tflops / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": measured_traffic(name, wl.kv_dtype)}
-    else:
-        roof = {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(name, wl.kv_dtype)}
-    flags = dec.flags()
-    line = {
-        "metric": "MLA decode TFLOP/s + effective KV GB/s (% roofline), B=64 H=128 L=4096 bf16",
-        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "warmup_note": f"{warm_total} untimed steps in all: the W asked for, then more until the GPU had been "
-                       f"busy {args.warm_seconds} s (clock ramp-up from idle)",
-        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": name, "batch": wl.batch, "heads": wl.num_heads, "seqlen_q": wl.s_q,
-                   "seqlens_sum": int(wl.seqlens.sum()), "kv_dtype": wl.kv_dtype, "page": 64, "cache_copies": copies},
+    res = {
+        "workload": name, "batch": wl.batch, "heads": wl.num_heads, "seqlen_q": wl.s_q, "causal": wl.causal,
+        "seqlens_sum": int(wl.seqlens.sum()), "kv_dtype": wl.kv_dtype, "page": 64, "cache_copies": copies,
+        "steps": steps, "warmup_steps_total": warm_total, "ms_per_step": round(ms_per_step, 5),
+        "step_ms": percentiles(blocks), "ms_per_step_with_plan": round(ms_per_step + plan_ms, 5),
+        "tflops": round(tflops, 2), "tflops_frac_mfma": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
         "kv_gbps": round(kv_gbps, 1), "kv_frac_hbm": round(kv_gbps / HBM_PEAK_GBPS, 4),
-        "tflops_frac_mfma": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
-        "kernel_ms": {"plan": round(float(np.mean(plan_ms)), 5), "decode": round(dec_avg, 5),
-                      "combine": round(float(np.mean(comb_ms)), 5)},
-        "kernel_timing": f"decode: HIP events inside the timed region on every {every}th step "
-                         f"({len(dec_ms)} launches); plan, combine: a separate pass after it",
-        "roofline": roof,
+        "gflop": round(flops / 1e9, 3), "kv_mb": round(kv_bytes / 1e6, 2), "alg_mb": round(alg_bytes / 1e6, 2),
+        "kernel_ms": {"decode": round(dec_ms, 5), "combine": round(comb_ms, 5), "plan": round(plan_ms, 5)},
+        "roofline": roofline_of(flops, alg_bytes, dec_ms, measured_traffic(name, wl.kv_dtype)),
+        "warm_single_copy": {"ms_per_step": round(warm1_ms, 5),
+                             "tflops": round(flops / (warm1_ms * 1e-3) / 1e12, 2),
+                             "note": "one cache copy reused every step: partly served by the last-level cache"},
         "flags": flags,
     }
+    if parity_rows:
+        rng = np.random.default_rng(123)
+        total = wl.batch * wl.s_q * wl.num_heads
+        rows = np.unique(np.concatenate([rng.integers(0, total, parity_rows), [0, total - 1]])).astype(np.int64)
+        ro, rl, _ = oracle_rows(wl, rows)
+        res["parity"] = parity(M, W, out_np, lse_np, rows, ro, rl, bf16_tol=not fp8)
+    del kvs, kss
+    return res, wl, out_np, lse_np
+
+
+OTHER_CONFIGS = ("ragged_b128_h128_l128_32768", "mtp_b32_h128_sq2_l8192", "fp8_b128_h128_l16384")
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU (a single MI355X); --gpus must be 1"}))
+        return 2
+    if args.copy_probe:
+        return copy_probe()
+    import torch
+    import workloads as W
+    import mla_latent_kv_fwd_amd as M
+
+    name = args.config or W.HEADLINE
+    main_res, wl, out_np, lse_np = measure(torch, M, W, name, steps=args.steps, warmup=args.warmup,
+                                           warm_seconds=args.warm_seconds, copies=args.copies, block=args.block,
+                                           roof_launches=args.roofline_launches)
+    r = main_res
+    line = {
+        "metric": "MLA decode TFLOP/s + effective KV GB/s (% roofline), B=64 H=128 L=4096 bf16",
+        "value": r["tflops"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "warmup_note": f"{r['warmup_steps_total']} untimed steps in all: the W asked for, then more until the GPU "
+                       f"had been busy {args.warm_seconds} s (clock ramp-up from idle)",
+        "ms_per_step": r["ms_per_step"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {k: r[k] for k in ("workload", "batch", "heads", "seqlen_q", "seqlens_sum", "kv_dtype", "page",
+                                     "cache_copies")},
+        "step": "decode + combine of one layer; the plan runs once per model step (kernel_ms.plan)",
+        "step_ms": r["step_ms"], "ms_per_step_with_plan": r["ms_per_step_with_plan"],
+        "kv_gbps": r["kv_gbps"], "kv_frac_hbm": r["kv_frac_hbm"], "tflops_frac_mfma": r["tflops_frac_mfma"],
+        "kernel_ms": r["kernel_ms"],
+        "kernel_timing": f"decode: {max(100, args.roofline_launches)} back-to-back launches between one HIP event "
+                         "pair on its stream; plan, combine: 50 back-to-back launches each",
+        "roofline": r["roofline"], "warm_single_copy": r["warm_single_copy"], "flags": r["flags"],
+    }
+    if not args.no_cpu:
+        cb, (rows, ro, rl) = cpu_baseline(wl, args.cpu_seconds)
+        line["cpu_baseline"] = cb
+        line["parity"] = parity(M, W, out_np, lse_np, rows, ro, rl, bf16_tol=wl.kv_dtype == "bf16")
+    del wl, out_np, lse_np
+    if not args.no_configs and args.config is None:
+        line["configs"] = {}
+        for cname in OTHER_CONFIGS:
+            cres, *_ = measure(torch, M, W, cname, steps=args.config_steps, warmup=5, warm_seconds=0.1,
+                               block=args.block, roof_launches=100, parity_rows=None if args.no_cpu else 64)
+            line["configs"][cname] = cres
     if not args.no_proj:
-        del kvs, kss
-        line["projections"] = bench_projections(torch, M, W, wl.batch * wl.s_q, wl.num_heads)
+        line["projections"] = bench_projections(torch, M, W, r["batch"] * r["seqlen_q"], r["heads"])
     if not args.no_prefill:
         line["prefill"] = bench_prefill(torch, M, W, args.prefill)
-    if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(line), flush=True)
     return 0
 

@@ -123,7 +123,7 @@ def _check_rows(got_o, got_l, ref_o, ref_l, what, lse_bound=None):
     seen = ~empty
     err = np.abs(got_o - ref_o)[seen]
     rel = np.linalg.norm(err) / max(np.linalg.norm(ref_o[seen]), 1e-30)
-    lerr = np.abs(got_l - ref_l)[seen]
+    lerr = np.abs(got_l[seen] - ref_l[seen])   # only rows that see a key: no -inf - -inf
     lb = LSE_MAX_ABS if lse_bound is None else lse_bound[seen]
     _say(f"{what}: out max-abs {err.max():.3e} rel-L2 {rel:.3e}  lse max-abs {lerr.max():.3e} "
          f"(worst lse err/bound {(lerr / lb).max():.3f}; {empty.sum()} empty rows)")
