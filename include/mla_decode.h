@@ -60,7 +60,8 @@ typedef enum {
   MLA_ERR_INVALID_ARG = -1,          /* null pointer, negative or inconsistent size */
   MLA_ERR_UNSUPPORTED = -2,          /* valid, but outside what the kernels implement */
   MLA_ERR_WORKSPACE_TOO_SMALL = -3,  /* workspace_bytes below the size query's answer */
-  MLA_ERR_HIP = -4                   /* a HIP runtime call or kernel launch failed */
+  MLA_ERR_HIP = -4,                  /* a HIP runtime call or kernel launch failed */
+  MLA_ERR_SCRATCH_TOO_SMALL = -5     /* mla_decode_noalloc: the step needs more than its fixed scratch */
 } mla_status;
 
 /* Cache element type ("MLA inference ...": FlashMLA paragraph and exercise 2 --
@@ -153,6 +154,28 @@ int mla_splitkv_combine(const mla_decode_params* p, const void* workspace, size_
  * workspace (waits for `stream` first).  *flags receives the bits.
  */
 int mla_workspace_flags(const void* workspace, uint32_t* flags, void* stream);
+
+/*
+ * For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc: one whole
+ * decode step (the split plan, mla_decode_fwd and mla_splitkv_combine) with its
+ * workspace in a fixed array of MLA_NOALLOC_SCRATCH_BYTES that the library
+ * holds on every GPU it runs on until the process ends.  Nothing is allocated:
+ * no hipMalloc, no hipFree, no allocating library call.  The arguments are those
+ * of mla_decode_fwd without the workspace; results are the same bits.
+ *
+ * Returns MLA_ERR_SCRATCH_TOO_SMALL, before anything is enqueued, when the
+ * step's workspace (the size mla_get_workspace reports for p) exceeds the
+ * array: with the default workgroup count that is about 65 MiB at any batch up
+ * to 8192 and any s_q * num_heads, so only a large explicit num_workgroups is
+ * rejected.  Every call on one GPU uses that GPU's one array, which keeps the
+ * last call's plan and partial results: calls ordered on one stream are safe;
+ * calls that overlap on one GPU (other streams, other threads) race.  The flag
+ * bits of mla_workspace_flags are not reported for this path.
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES ((size_t)80 << 20)
+int mla_decode_noalloc(const mla_decode_params* p, const void* q, const void* kv_cache, const float* kv_scale,
+                       const int32_t* block_table, const int32_t* seqlens, void* out, float* lse, void* stream);
 
 /* Static description of a status code. */
 const char* mla_status_string(int status);

@@ -26,6 +26,8 @@ MLA_ERR_INVALID_ARG = -1
 MLA_ERR_UNSUPPORTED = -2
 MLA_ERR_WORKSPACE_TOO_SMALL = -3
 MLA_ERR_HIP = -4
+MLA_ERR_SCRATCH_TOO_SMALL = -5
+MLA_NOALLOC_SCRATCH_BYTES = 80 << 20
 MLA_KV_BF16 = 0
 MLA_KV_FP8_E4M3FN = 1
 MLA_FLAG_SEQLEN_CLAMPED = 0x1
@@ -39,7 +41,8 @@ SOFTMAX_SCALE = 1.0 / math.sqrt(128 + 64)
 
 EXPORTED_SYMBOLS = ("mla_get_workspace", "mla_decode_fwd", "mla_splitkv_combine", "mla_workspace_flags",
                     "mla_status_string", "mla_absorb_q", "mla_project_out", "mla_expand_kv",
-                    "mla_prefill_attention", "mla_lse_merge", "mla_prefill_workspace_size", "mla_chunked_prefill")
+                    "mla_prefill_attention", "mla_lse_merge", "mla_prefill_workspace_size", "mla_chunked_prefill",
+                    "mla_decode_noalloc")
 D_NOPE, D_ROPE, D_LATENT, D_V = 128, 64, 512, 128
 
 
@@ -105,6 +108,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_get_workspace.argtypes = [pp, vp, vp, ctypes.POINTER(sz), vp]
     lib.mla_decode_fwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
     lib.mla_splitkv_combine.argtypes = [pp, vp, sz, vp, vp, vp]
+    lib.mla_decode_noalloc.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.mla_workspace_flags.argtypes = [vp, ctypes.POINTER(ctypes.c_uint32), vp]
     lib.mla_status_string.argtypes = [ctypes.c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
@@ -154,6 +158,13 @@ def mla_splitkv_combine(params: DecodeParams, workspace_ptr: int, workspace_byte
     _check("mla_splitkv_combine", load_library().mla_splitkv_combine(
         ctypes.byref(params), workspace_ptr or None, workspace_bytes, out_ptr or None, lse_ptr or None,
         stream or None))
+
+
+def mla_decode_noalloc(params: DecodeParams, q_ptr: int, kv_ptr: int, kv_scale_ptr: int, block_table_ptr: int,
+                       seqlens_ptr: int, out_ptr: int, lse_ptr: int, stream: int = 0) -> None:
+    _check("mla_decode_noalloc", load_library().mla_decode_noalloc(
+        ctypes.byref(params), q_ptr or None, kv_ptr or None, kv_scale_ptr or None, block_table_ptr or None,
+        seqlens_ptr or None, out_ptr or None, lse_ptr or None, stream or None))
 
 
 def mla_workspace_flags(workspace_ptr: int, stream: int = 0) -> int:

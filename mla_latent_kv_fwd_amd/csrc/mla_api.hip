@@ -120,6 +120,25 @@ PrefillLayout prefill_layout(const mla_prefill_params* p) {
   return l;
 }
 
+// The no-allocation path's workspace: one fixed array per GPU, in the code
+// object's zero-initialised data.  In host code `scratch` names a host-side
+// stand-in, never the device memory: the device address comes from
+// hipGetSymbolAddress, taken once per device with that device current, and
+// only that address is passed to kernels.
+static __device__ __align__(256) unsigned char scratch[MLA_NOALLOC_SCRATCH_BYTES];
+
+void* scratch_address(int dev) {
+  static std::once_flag once[kMaxDevices];
+  static void* addr[kMaxDevices];
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::call_once(once[dev], [dev] {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) ptr = nullptr;
+    addr[dev] = ptr;
+  });
+  return addr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -131,6 +150,7 @@ const char* mla_status_string(int status) {
     case MLA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
     case MLA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case MLA_ERR_HIP: return "HIP runtime error";
+    case MLA_ERR_SCRATCH_TOO_SMALL: return "step needs more than the fixed no-allocation scratch";
     default: return "unknown status";
   }
 }
@@ -193,6 +213,29 @@ int mla_decode_fwd(const mla_decode_params* p, const void* q, const void* kv_cac
   a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
   if (launch_decode(a, p->kv_dtype == MLA_KV_FP8_E4M3FN, (hipStream_t)stream) != hipSuccess) return MLA_ERR_HIP;
   return MLA_OK;
+}
+
+int mla_decode_noalloc(const mla_decode_params* p, const void* q, const void* kv_cache, const float* kv_scale,
+                       const int32_t* block_table, const int32_t* seqlens, void* out, float* lse, void* stream) {
+  int st = validate(p);
+  if (st != MLA_OK) return st;
+  if (!q || !kv_cache || !block_table || !seqlens || !out || !lse) return MLA_ERR_INVALID_ARG;
+  int nwg = 0;
+  if ((st = resolve_nwg(p, &nwg)) != MLA_OK) return st;
+  const Layout lay = make_layout(p->batch, p->seqlen_q * p->num_heads, nwg);
+  if (lay.total > MLA_NOALLOC_SCRATCH_BYTES) return MLA_ERR_SCRATCH_TOO_SMALL;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MLA_ERR_HIP;
+  void* ws = scratch_address(dev);
+  if (!ws) return MLA_ERR_HIP;
+  // The plan writes every plan entry and header field the decode reads, and the
+  // decode writes every partial the combine reads: nothing needs clearing.
+  size_t nbytes = lay.total;
+  if ((st = mla_get_workspace(p, seqlens, ws, &nbytes, stream)) != MLA_OK) return st;
+  if ((st = mla_decode_fwd(p, q, kv_cache, kv_scale, block_table, seqlens, ws, lay.total, out, lse, stream)) !=
+      MLA_OK)
+    return st;
+  return mla_splitkv_combine(p, ws, lay.total, out, lse, stream);
 }
 
 int mla_splitkv_combine(const mla_decode_params* p, const void* workspace, size_t workspace_bytes, void* out,
