@@ -381,6 +381,7 @@ def measure(torch, M, W, name, *, steps, warmup, warm_seconds, copies=0, block=1
     warm_total = warmup + keep_busy(torch, step, seconds=warm_seconds, min_calls=0)
 
     # Timed region: exactly `steps` steps, synchronised on both sides; an event at every block boundary.
+    block = max(1, min(block, steps))
     nblk = max(1, steps // block)
     marks = [ev() for _ in range(nblk + 1)]
     torch.cuda.synchronize()

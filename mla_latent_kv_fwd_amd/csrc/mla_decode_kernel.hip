@@ -36,9 +36,11 @@
 //     test is on each lane's own maximum (one ballot); the cross-lane row
 //     maximum is formed only when it fires.  The scale is folded into the
 //     exponent's FMA.
-//   * The LDS reads of the two contractions are pinned one (scores) and two
-//     (values) MFMAs ahead with scheduling barriers: without them the compiler
-//     sinks each read to its use and every MFMA waits a full LDS latency.
+//   * The LDS reads of the two contractions are pinned two K-steps (scores) and
+//     three dim tiles (values) ahead with scheduling barriers: without them the
+//     compiler sinks each read to its use and every MFMA waits a full LDS
+//     latency.  The registers for that depth come from rebuilding the loading
+//     waves' per-lane load offsets at each issue instead of keeping them live.
 //   * Tokens past the request's length are never loaded (their rows are
 //     replaced by the last valid token) and are masked to -inf, so stale or NaN
 //     bytes in a partly used last page cannot reach the output.
@@ -285,9 +287,6 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
   const bool row_ok = row < a.rows;
   const int qi = row_ok ? row / a.num_heads : 0;   // which new token this row belongs to
   const bool loader = wave < kLoadWaves;
-  int voff_full[kLoadsPerWave];   // this lane's load offsets for a full chunk
-#pragma unroll
-  for (int i = 0; i < kLoadsPerWave; i++) voff_full[i] = dma_off(i, wave & (kLoadWaves - 1), lane, kChunk);
 
   // Per-lane LDS byte offsets within a slot.
   // QK A-operand: token 16tt + n, logical granule 4k + q -> physical 8(k>>1) + ((4(k&1)) ^ y).
@@ -374,15 +373,13 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
       const char* src = kv + ((size_t)page * kPageSize + (t0 % kPageSize)) * kRowBytes;
       const int valid = t_hi - t0 < kChunk ? t_hi - t0 : kChunk;
       const uint32_t m0 = smem_addr + (c % kSlots) * kSlotBytes + wave * 1024;
-      if (valid == kChunk) {
-        dma_chunk(src, m0, voff_full);
-      } else {   // a request's last, partial chunk
-        const int l = opaque_lane();
-        int voff[kLoadsPerWave];
+      // Per-lane offsets rebuilt from the lane at each issue (a few VALU on the
+      // loading waves) rather than nine registers kept live.
+      const int l = opaque_lane();
+      int voff[kLoadsPerWave];
 #pragma unroll
-        for (int i = 0; i < kLoadsPerWave; i++) voff[i] = dma_off(i, wave, l, valid);
-        dma_chunk(src, m0, voff);
-      }
+      for (int i = 0; i < kLoadsPerWave; i++) voff[i] = dma_off(i, wave, l, valid);
+      dma_chunk(src, m0, voff);
     };
     // Queries and window have landed before the first readlane.  Waiting here,
     // outside the issue loop, leaves the compiler nothing of its own to wait for
@@ -409,23 +406,27 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
       const int t0 = t_lo + c * kChunk;
 
       // S^T[token][row] over the 576 dims, two 16-token tiles.  Fragments are read
-      // one K-step ahead so each MFMA's operands are already in flight.
+      // two K-steps ahead so each MFMA's operands are already in flight.
       f32x4_t s0 = f32x4_t{}, s1 = f32x4_t{};
-      bf16x8_t a0 = lds_read_b128(slot + qk_off0);
-      bf16x8_t a1 = lds_read_b128(slot + 16 * kRowBytes + qk_off0);
+      auto qk_off = [&](int kk) { return ((kk & 1) ? qk_off1 : qk_off0) + (kk >> 1) * 128; };
+      bf16x8_t a0 = lds_read_b128(slot + qk_off(0));
+      bf16x8_t a1 = lds_read_b128(slot + 16 * kRowBytes + qk_off(0));
+      bf16x8_t b0 = lds_read_b128(slot + qk_off(1));
+      bf16x8_t b1 = lds_read_b128(slot + 16 * kRowBytes + qk_off(1));
 #pragma unroll
       for (int k = 0; k < kKSteps; k++) {
-        bf16x8_t n0 = a0, n1 = a1;
-        if (k + 1 < kKSteps) {
-          const int off = (((k + 1) & 1) ? qk_off1 : qk_off0) + ((k + 1) >> 1) * 128;
-          n0 = lds_read_b128(slot + off);
-          n1 = lds_read_b128(slot + 16 * kRowBytes + off);
+        bf16x8_t n0 = b0, n1 = b1;
+        if (k + 2 < kKSteps) {
+          n0 = lds_read_b128(slot + qk_off(k + 2));
+          n1 = lds_read_b128(slot + 16 * kRowBytes + qk_off(k + 2));
         }
         s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[k], s0, 0, 0, 0);
         s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[k], s1, 0, 0, 0);
-        a0 = n0;
-        a1 = n1;
-        // keep step k+1's reads ahead of step k's MFMAs
+        a0 = b0;
+        a1 = b1;
+        b0 = n0;
+        b1 = n1;
+        // keep steps k+1 and k+2's reads ahead of step k's MFMAs
         __builtin_amdgcn_sched_barrier(0);
       }
 
@@ -465,21 +466,22 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
       }
 
       // O^T[dim][row] += V^T[dim][token] . P^T[token][row], 32 tiles of 16 dims,
-      // V^T fragments read two tiles ahead.
+      // V^T fragments read three tiles ahead.
       auto read_v = [&](int d) {
         const int off = pv_off[d & 3] + (d >> 2) * 128;
         const i16x4_t lo = lds_read_tr16(slot + off);
         const i16x4_t hi = lds_read_tr16(slot + 16 * kRowBytes + off);
         return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       };
-      bf16x8_t v0 = read_v(0), v1 = read_v(1);
+      bf16x8_t v0 = read_v(0), v1 = read_v(1), v2 = read_v(2);
 #pragma unroll
       for (int d = 0; d < kDimTiles; d++) {
-        bf16x8_t v2 = v1;
-        if (d + 2 < kDimTiles) v2 = read_v(d + 2);
+        bf16x8_t v3 = v2;
+        if (d + 3 < kDimTiles) v3 = read_v(d + 3);
         o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v0, pb, o[d], 0, 0, 0);
         v0 = v1;
         v1 = v2;
+        v2 = v3;
         __builtin_amdgcn_sched_barrier(0);
       }
     }
