@@ -72,6 +72,20 @@ typedef enum {
   MLA_KV_FP8_E4M3FN = 1   /* cache holds OCP E4M3FN codes; value = decode(code) * kv_scale[page][slot] */
 } mla_kv_dtype;
 
+/* How an FP8 cache is multiplied (no effect on a bf16 cache). */
+typedef enum {
+  MLA_FP8_PATH_EXACT = 0,  /* codes widened to bf16 exactly, bf16 MFMAs, scale applied in fp32: the bf16
+                              path's rounding only (one bf16 rounding of each softmax weight) */
+  MLA_FP8_PATH_MFMA = 1    /* both products on E4M3 MFMAs ("MLA inference ...": Exercises, answer 2 -- FP8
+                              tensor cores for the absorbed decode, with careful handling of precision):
+                              q~ kept as a per-row scale times a sum of two E4M3 numbers (about 2^-8 of
+                              q~), and each softmax weight times its token's scale times a power of two
+                              rounded once to E4M3 (3 mantissa bits) for the value product; the running
+                              maximum is raised whenever a score passes it by a factor 2, so the weights
+                              stay in E4M3's normal range.  Relative L2 error of the output about 1.5e-2 on
+                              random inputs, against the oracle's exact result */
+} mla_fp8_path;
+
 /* Bits reported by mla_workspace_flags(). */
 #define MLA_FLAG_SEQLEN_CLAMPED 0x1  /* some seqlens[b] was < seqlen_q or > max_blocks_per_seq * page_size */
 #define MLA_FLAG_BAD_BLOCK      0x2  /* some referenced block-table entry was outside [0, num_pages) */
@@ -93,6 +107,7 @@ typedef struct {
   float softmax_scale;         /* > 0, e.g. 1/sqrt(192) */
   int32_t num_workgroups;      /* 0: one persistent workgroup per compute unit (the default);
                                   > 0: use that many (tests use it to force other split plans) */
+  int32_t fp8_path;            /* an mla_fp8_path; must be MLA_FP8_PATH_EXACT for a bf16 cache */
 } mla_decode_params;
 
 /*

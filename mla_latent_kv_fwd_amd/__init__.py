@@ -33,6 +33,8 @@ MLA_KV_FP8_E4M3FN = 1
 MLA_FLAG_SEQLEN_CLAMPED = 0x1
 MLA_FLAG_BAD_BLOCK = 0x2
 MLA_FLAG_BAD_PLAN = 0x4
+MLA_FP8_PATH_EXACT = 0
+MLA_FP8_PATH_MFMA = 1
 
 HEAD_DIM_QK = 576
 HEAD_DIM_V = 512
@@ -57,7 +59,8 @@ class DecodeParams(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("seqlen_q", ctypes.c_int32), ("num_heads", ctypes.c_int32),
                 ("head_dim_qk", ctypes.c_int32), ("head_dim_v", ctypes.c_int32), ("page_size", ctypes.c_int32),
                 ("num_pages", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
-                ("causal", ctypes.c_int32), ("softmax_scale", ctypes.c_float), ("num_workgroups", ctypes.c_int32)]
+                ("causal", ctypes.c_int32), ("softmax_scale", ctypes.c_float), ("num_workgroups", ctypes.c_int32),
+                ("fp8_path", ctypes.c_int32)]
 
 
 class ProjParams(ctypes.Structure):
@@ -86,10 +89,10 @@ def make_prefill_params(*, num_heads, num_new, seqlen, num_pages, max_blocks, ch
 
 
 def make_params(*, batch, seqlen_q, num_heads, num_pages, max_blocks_per_seq, kv_dtype=MLA_KV_BF16, causal=False,
-                softmax_scale=SOFTMAX_SCALE, num_workgroups=0, head_dim_qk=HEAD_DIM_QK, head_dim_v=HEAD_DIM_V,
-                page_size=PAGE_SIZE) -> DecodeParams:
+                softmax_scale=SOFTMAX_SCALE, num_workgroups=0, fp8_path=MLA_FP8_PATH_EXACT, head_dim_qk=HEAD_DIM_QK,
+                head_dim_v=HEAD_DIM_V, page_size=PAGE_SIZE) -> DecodeParams:
     return DecodeParams(batch, seqlen_q, num_heads, head_dim_qk, head_dim_v, page_size, num_pages,
-                        max_blocks_per_seq, kv_dtype, int(bool(causal)), softmax_scale, num_workgroups)
+                        max_blocks_per_seq, kv_dtype, int(bool(causal)), softmax_scale, num_workgroups, fp8_path)
 
 
 _lib = None
@@ -356,12 +359,13 @@ class MlaDecode:
     """
 
     def __init__(self, *, batch, seqlen_q, num_heads, num_pages, max_blocks_per_seq, kv_dtype=MLA_KV_BF16,
-                 causal=False, softmax_scale=SOFTMAX_SCALE, num_workgroups=0, device="cuda"):
+                 causal=False, softmax_scale=SOFTMAX_SCALE, num_workgroups=0, fp8_path=MLA_FP8_PATH_EXACT,
+                 device="cuda"):
         import torch
         self.torch = torch
         self.params = make_params(batch=batch, seqlen_q=seqlen_q, num_heads=num_heads, num_pages=num_pages,
                                   max_blocks_per_seq=max_blocks_per_seq, kv_dtype=kv_dtype, causal=causal,
-                                  softmax_scale=softmax_scale, num_workgroups=num_workgroups)
+                                  softmax_scale=softmax_scale, num_workgroups=num_workgroups, fp8_path=fp8_path)
         self.device = _resolve_device(device)
         self.workspace_bytes = mla_get_workspace(self.params)
         # 256-byte aligned: the caching allocator hands out 512-byte aligned blocks.

@@ -40,6 +40,8 @@ int validate(const mla_decode_params* p) {
   if (p->num_workgroups < 0) return MLA_ERR_INVALID_ARG;
   if (!(p->softmax_scale > 0.f) || !isfinite(p->softmax_scale)) return MLA_ERR_INVALID_ARG;
   if (p->kv_dtype != MLA_KV_BF16 && p->kv_dtype != MLA_KV_FP8_E4M3FN) return MLA_ERR_INVALID_ARG;
+  if (p->fp8_path != MLA_FP8_PATH_EXACT && p->fp8_path != MLA_FP8_PATH_MFMA) return MLA_ERR_INVALID_ARG;
+  if (p->fp8_path == MLA_FP8_PATH_MFMA && p->kv_dtype != MLA_KV_FP8_E4M3FN) return MLA_ERR_INVALID_ARG;
   if (p->head_dim_qk != kHeadDimQK || p->head_dim_v != kHeadDimV || p->page_size != kPageSize)
     return MLA_ERR_UNSUPPORTED;
   if (p->seqlen_q > kMaxSeqlenQ || p->num_heads > kMaxHeads) return MLA_ERR_UNSUPPORTED;
@@ -211,7 +213,10 @@ int mla_decode_fwd(const mla_decode_params* p, const void* q, const void* kv_cac
   a.max_blocks = p->max_blocks_per_seq;
   a.causal = p->causal ? 1 : 0;
   a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
-  if (launch_decode(a, p->kv_dtype == MLA_KV_FP8_E4M3FN, (hipStream_t)stream) != hipSuccess) return MLA_ERR_HIP;
+  const hipError_t e = p->fp8_path == MLA_FP8_PATH_MFMA
+                           ? launch_decode_fp8_mfma(a, (hipStream_t)stream)
+                           : launch_decode(a, p->kv_dtype == MLA_KV_FP8_E4M3FN, (hipStream_t)stream);
+  if (e != hipSuccess) return MLA_ERR_HIP;
   return MLA_OK;
 }
 

@@ -25,6 +25,7 @@ struct DecodeArgs {
 hipError_t launch_plan(const int32_t* seqlens, void* ws, const Layout& lay, int batch, int seqlen_q, int rows,
                        int nwg, int max_blocks, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, bool fp8, hipStream_t stream);
+hipError_t launch_decode_fp8_mfma(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_combine(const char* ws, const Layout& lay, int batch, int rows, int nwg, int max_blocks,
                           uint16_t* out, float* lse, hipStream_t stream);
 hipError_t launch_absorb_q(const uint16_t* q_nope, const uint16_t* q_rope, const uint16_t* w_uk, uint16_t* q_tilde,

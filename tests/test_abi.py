@@ -77,6 +77,9 @@ def test_size_query_needs_no_device(lib):
     ("page_size", 16, M.MLA_ERR_UNSUPPORTED),
     ("num_heads", 129, M.MLA_ERR_UNSUPPORTED),
     ("seqlen_q", 9, M.MLA_ERR_UNSUPPORTED),
+    ("fp8_path", 2, M.MLA_ERR_INVALID_ARG),
+    ("fp8_path", -1, M.MLA_ERR_INVALID_ARG),
+    ("fp8_path", 1, M.MLA_ERR_INVALID_ARG),      # the E4M3 route needs an FP8 cache
 ])
 def test_bad_params_are_rejected(lib, field, value, status):
     p = _params()

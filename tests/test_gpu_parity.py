@@ -58,12 +58,12 @@ def to_gpu(torch, wl):
     return q, kv, ks, bt, sl
 
 
-def run_gpu(torch, M, wl, num_workgroups=0, tensors=None):
+def run_gpu(torch, M, wl, num_workgroups=0, tensors=None, fp8_path=0):
     q, kv, ks, bt, sl = tensors if tensors is not None else to_gpu(torch, wl)
     dec = M.MlaDecode(batch=wl.batch, seqlen_q=wl.s_q, num_heads=wl.num_heads, num_pages=wl.num_pages,
                       max_blocks_per_seq=wl.block_table.shape[1], causal=wl.causal,
                       kv_dtype=M.MLA_KV_FP8_E4M3FN if wl.kv_dtype == "fp8_e4m3fn" else M.MLA_KV_BF16,
-                      softmax_scale=float(wl.softmax_scale), num_workgroups=num_workgroups)
+                      softmax_scale=float(wl.softmax_scale), num_workgroups=num_workgroups, fp8_path=fp8_path)
     out, lse = dec(q, kv, bt, sl, ks)
     torch.cuda.synchronize()
     flags = dec.flags()
