@@ -79,9 +79,13 @@ constexpr int kXBufBytes = (kXTok + kXW) * kXK * 2;   // 24 KiB
 constexpr int kXLoads = kXBufBytes / 1024 / (kXThreads / 64);   // 6 one-KiB loads per wave per stage
 static_assert(kXLoads * 1024 * (kXThreads / 64) == kXBufBytes, "");
 static_assert(2 * 128 * 272 <= kXBufs * kXBufBytes, "the staged output tile fits in the ring");
-// Operand row r of a stage (64 bytes): granule j stored at j ^ ((r >> 2) & 3), so 16
-// lanes reading one granule of 16 consecutive rows hit 16 bank groups.
-__device__ __forceinline__ int xp_off(int r, int j) { return r * 64 + ((j ^ ((r >> 2) & 3)) << 4); }
+// Operand row r of a stage (64 bytes): granule j stored at j ^ xp_swz(r).  The
+// fragment read (lane (g, q): granule g of row 16 i + q) runs at the LDS's full
+// rate with this map; the map j ^ ((r >> 2) & 3), which spreads 16 rows over 16
+// 16-byte bank groups, ran at 57% of it (timed over all 256 linear maps of the
+// row's low 4 bits to 2 bits; several reach the full rate).
+__device__ __forceinline__ int xp_swz(int r) { return ((r >> 2) & 1) | ((((r >> 1) ^ (r >> 2)) & 1) << 1); }
+__device__ __forceinline__ int xp_off(int r, int j) { return r * 64 + ((j ^ xp_swz(r)) << 4); }
 
 // One 16-byte direct-to-LDS load per lane from a per-lane 64-bit address: lane i
 // writes LDS[m0 + 16 i].  The wait states cover M0 written from a VALU-produced
@@ -140,7 +144,7 @@ __global__ __launch_bounds__(kXThreads, 2) void mla_expand_kv_kernel(const uint1
   // Per-lane source rows of this wave's six loads of a stage: load i is block
   // b = 4 i + wave; lane granule G = 64 (b - first block of its tile) + lane is
   // row G / 4 of that tile, stored granule G % 4, which holds logical granule
-  // (G % 4) ^ ((row >> 2) & 3).
+  // (G % 4) ^ xp_swz(row).
   const uint16_t* wt = (is_k ? w_uk : w_uv);
   const char* src[kXLoads];
 #pragma unroll
@@ -149,7 +153,7 @@ __global__ __launch_bounds__(kXThreads, 2) void mla_expand_kv_kernel(const uint1
     const bool latent = is_k ? b >= lat_blk0 : b < w_blk0;
     const int G = 64 * (b - (latent ? lat_blk0 : w_blk0)) + lane;
     const int row = G >> 2;
-    const int j = (G & 3) ^ ((row >> 2) & 3);
+    const int j = (G & 3) ^ xp_swz(row);
     const uint16_t* p;
     if (latent) {
       int t = tile_t + row;
