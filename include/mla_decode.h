@@ -81,8 +81,8 @@ typedef enum {
                               q~ kept as a per-row scale times a sum of two E4M3 numbers (about 2^-8 of
                               q~), and each softmax weight times its token's scale times a power of two
                               rounded once to E4M3 (3 mantissa bits) for the value product; the running
-                              maximum is raised whenever a score passes it by a factor 2, so the weights
-                              stay in E4M3's normal range.  Relative L2 error of the output about 1.5e-2 on
+                              maximum is raised whenever a score passes it by a factor 8, so the weights
+                              that matter stay in E4M3's normal range.  Relative L2 error of the output about 1.5e-2 on
                               random inputs, against the oracle's exact result */
 } mla_fp8_path;
 

@@ -16,10 +16,14 @@
 //     value product: P'_t = E4M3(p_t scale_t 2^E), E a power of two per 128-token
 //     chunk chosen so that P' <= 448; the output is divided by 2^E at the end.  The
 //     normaliser sums the unrounded p_t.  The running maximum is rescaled as soon
-//     as a score exceeds it by a factor 2 (not 2^8 as in the exact route), so
-//     p <= 2 and small weights keep E4M3's full precision down to p ~ 2^-13: with
-//     2^8 of headroom, weights far below a new maximum fall into E4M3's subnormal
-//     range, where rounding is coarse and biased.
+//     as a score exceeds it by a factor 2^3 (not 2^8 as in the exact route), so
+//     p <= 8 and, E4M3's normal range spanning 2^14.8, weights down to p ~ 2^-11.8
+//     keep its full precision: with 2^8 of headroom, weights far below a new
+//     maximum fell into the subnormal range, where rounding is coarse and, for
+//     many equal weights, biased.  A smaller threshold costs time: every rescale
+//     inside a chunk folds the steps gathered so far into O with an extra value
+//     product (measured at the 128 x 16384 workload: factor 2, 573 us; 2^2, 554;
+//     2^3, 544; 2^4, 538).
 //
 // CDNA4 mapping.  8 waves x 16 query rows (all heads of one request), one
 // persistent workgroup per stretch of the split plan, lane = row, as in the exact
@@ -67,7 +71,7 @@ constexpr int kLoadsPerPageF = kPageSize * kGranF / 64;        // 36 one-KiB loa
 constexpr int kLoadsPerWaveF = 2 * kLoadsPerPageF / kWaves;    // 9
 constexpr int kLatBlocks = 4;                         // 128-dim blocks of the latent
 constexpr float kE4M3Max = 448.f;
-constexpr float kLazyRescaleF = 1.0f;                 // log2 of the largest p kept unrescaled
+constexpr float kLazyRescaleF = 3.0f;                 // log2 of the largest p kept unrescaled
 // The weights P' of a chunk's first three 32-token steps wait in LDS until the
 // value product (8 bytes per lane per step), keeping them out of the registers
 // during the score products.
@@ -326,8 +330,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_fp8_mfma_kernel(Decode
       const int t0 = t_lo + c * kChunkF;
       const int valid = t_hi - t0 < kChunkF ? t_hi - t0 : kChunkF;
 
-      // The P' factor of this chunk: 2^E <= 224 / max scale over its valid tokens,
-      // so p scale 2^E <= 448 for p <= 2.  E only decreases within a segment (O is
+      // The P' factor of this chunk: 2^E <= 56 / max scale over its valid tokens,
+      // so p scale 2^E <= 448 for p <= 8.  E only decreases within a segment (O is
       // rescaled by the exact power of two when it does).
       {
         const int ol = opaque_lane();
@@ -341,7 +345,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_fp8_mfma_kernel(Decode
         mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(mx), 0x1F | (4 << 10))));
         mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(mx), 0x1F | (8 << 10))));
         mx = row_max(mx);
-        const float f = mx > 0.f ? 224.f / mx : 0x1p100f;
+        const float f = mx > 0.f ? 56.f / mx : 0x1p100f;
         int e = (int)((__float_as_uint(f) >> 23) & 255) - 127;
         e = e > 100 ? 100 : (e < -100 ? -100 : e);
         e = __builtin_amdgcn_readfirstlane(e);   // the same in every lane
