@@ -76,7 +76,7 @@ def _latents(pw):
 
 # ------------------------------------------------------------------ expansion
 @pytest.mark.parametrize("H,L,t0,ntok", [(16, 700, 0, 700), (128, 300, 64, 200), (4, 5000, 1000, 4000),
-                                         (8, 130, 129, 1)])
+                                         (8, 130, 129, 1), (3, 1000, 100, 777), (1, 64, 0, 64), (127, 600, 37, 300)])
 def test_expand_kv_matches_oracle(torch, M, H, L, t0, ntok):
     pw = W.make_prefill_workload("exp", num_heads=H, num_new=1, seqlen=L, seed=H + L + t0)
     _say(f"expand_kv H={H} L={L} t0={t0} ntok={ntok}")
@@ -207,7 +207,8 @@ def _oracle_expand(pw, rows=None, heads=None):
 
 
 @pytest.mark.parametrize("H,n,L,chunk", [(16, 200, 1500, 256), (16, 300, 300, 128), (16, 300, 300, 4096),
-                                         (8, 64, 4000, 1024), (16, 1, 500, 128), (128, 96, 700, 256)])
+                                         (8, 64, 4000, 1024), (16, 1, 500, 128), (128, 96, 700, 256),
+                                         (5, 100, 900, 320)])
 def test_chunked_prefill_matches_expand_path(torch, M, H, n, L, chunk):
     pw = W.make_prefill_workload("pf", num_heads=H, num_new=n, seqlen=L, seed=3 * H + n + L)
     _say(f"chunked prefill H={H} n={n} L={L} chunk={chunk}")
