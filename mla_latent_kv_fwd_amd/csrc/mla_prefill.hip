@@ -31,6 +31,8 @@ typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 #define LDS_AS __attribute__((address_space(3)))
+// Read-only for the whole kernel: loads through it become scalar loads.
+#define CONST_AS __attribute__((address_space(4)))
 
 constexpr int kNope = 128, kRope = 64, kLat = 512, kDv = 128;
 constexpr int kQK = kNope + kRope;   // 192
@@ -146,6 +148,23 @@ __global__ __launch_bounds__(kXThreads, 2) void mla_expand_kv_kernel(const uint1
   // row G / 4 of that tile, stored granule G % 4, which holds logical granule
   // (G % 4) ^ xp_swz(row).
   const uint16_t* wt = (is_k ? w_uk : w_uv);
+  // The tile's tokens lie on at most three pages: their block-table entries are
+  // read once through the scalar cache (uniform loads), not once per lane.
+  const int pos_lo = t0 + tile_t;
+  const int pos_hi = t0 + (tile_t + kXTok - 1 < ntok - 1 ? tile_t + kXTok - 1 : ntok - 1);
+  const int pg_lo = __builtin_amdgcn_readfirstlane(pos_lo / kPage);
+  const int pg_hi = __builtin_amdgcn_readfirstlane(pos_hi / kPage);
+  const int32_t CONST_AS* btc = (const int32_t CONST_AS*)block_table;
+  int pages3[3];
+#pragma unroll
+  for (int u = 0; u < 3; u++) {
+    int pg = btc[pg_lo + u <= pg_hi ? pg_lo + u : pg_hi];
+    pages3[u] = (pg < 0 || pg >= num_pages) ? 0 : pg;
+  }
+  auto page_of = [&](int pos) {   // pos within [pos_lo, pos_hi]
+    const int d = pos / kPage - pg_lo;
+    return d == 0 ? pages3[0] : (d == 1 ? pages3[1] : pages3[2]);
+  };
   const char* src[kXLoads];
 #pragma unroll
   for (int i = 0; i < kXLoads; i++) {
@@ -159,9 +178,7 @@ __global__ __launch_bounds__(kXThreads, 2) void mla_expand_kv_kernel(const uint1
       int t = tile_t + row;
       t = t < ntok ? t : ntok - 1;
       const int pos = t0 + t;
-      int page = block_table[pos / kPage];
-      page = (page < 0 || page >= num_pages) ? 0 : page;
-      p = cache + ((size_t)page * kPage + pos % kPage) * kCacheRow;
+      p = cache + ((size_t)page_of(pos) * kPage + pos % kPage) * kCacheRow;
     } else {
       int h = 2 * hp + (row >> 7);
       h = h < H ? h : H - 1;
@@ -271,9 +288,7 @@ __global__ __launch_bounds__(kXThreads, 2) void mla_expand_kv_kernel(const uint1
       bf16x8_t v = bf16x8_t{};
       if (t < ntok) {
         const int pos = t0 + t;
-        int page = block_table[pos / kPage];
-        page = (page < 0 || page >= num_pages) ? 0 : page;
-        v = *reinterpret_cast<const bf16x8_t*>(cache + ((size_t)page * kPage + pos % kPage) * kCacheRow + kLat +
+        v = *reinterpret_cast<const bf16x8_t*>(cache + ((size_t)page_of(pos) * kPage + pos % kPage) * kCacheRow + kLat +
                                                 8 * part);
       }
       __builtin_nontemporal_store(__builtin_bit_cast(i32x4_t, v),
