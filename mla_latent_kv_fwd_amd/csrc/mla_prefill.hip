@@ -8,8 +8,9 @@
 // All contractions run on v_mfma_f32_16x16x32_bf16 with fp32 accumulation.
 //
 // Expansion is a GEMM [tokens x 512] x [512 x (H x 256)] with the latent rows
-// gathered through the block table: 128-token by two-head tiles streamed through
-// LDS with direct-to-LDS loads, two workgroups per CU (details at the kernel).
+// gathered through the block table: each workgroup keeps one head's weights of
+// one product in registers and streams 128-token tiles of the latent through LDS
+// with direct-to-LDS loads, one workgroup per CU (details at the kernel).
 //
 // Attention keeps the decode kernel's orientation -- scores as S^T = K . q^T,
 // lane = query -- with 32 queries per wave, so every K or V^T fragment read
@@ -44,6 +45,14 @@ constexpr float kLn2 = 0.69314718055994531f;
 __device__ __forceinline__ bf16x8_t lds_b128(const char LDS_AS* p) { return *reinterpret_cast<const bf16x8_t LDS_AS*>(p); }
 __device__ __forceinline__ void lds_w128(char LDS_AS* p, bf16x8_t v) { *reinterpret_cast<bf16x8_t LDS_AS*>(p) = v; }
 
+// The lane index, hidden from the optimiser: per-lane address terms derived from
+// it are recomputed where they are used rather than kept live across loops.
+__device__ __forceinline__ int opaque_lane() {
+  int l = __lane_id();
+  asm volatile("" : "+v"(l));
+  return l;
+}
+
 __device__ __forceinline__ float row_max(float x) {
   auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -60,34 +69,44 @@ __device__ __forceinline__ float row_sum(float x) {
 // ===========================================================================
 // Expansion
 // ===========================================================================
-// One GEMM per chunk: [tokens x 512] x [512 x (H x 256)].  A workgroup of four
-// waves owns a macro tile of 128 tokens by two heads' 128 outputs of one product
-// (256 weight rows), and each wave a 128 x 64 part of it, so a fragment read from
-// LDS feeds four or eight MFMAs.  The two operand tiles (32 latent columns of
-// 128 token rows and 256 weight rows per stage, 24 KiB) stream HBM -> LDS with
-// direct-to-LDS loads into a ring of three stages, two in flight; one barrier
-// per stage of 32 MFMAs per wave.  Two workgroups share a compute unit and cover
-// each other's load latency and epilogue.  The latent rows are gathered through
-// the block table when the per-lane row addresses are set up; rows past the
-// range repeat the last token and their outputs are written as zeros.  The
-// output tile is staged in LDS and leaves in whole rows with non-temporal stores.
-constexpr int kXTok = 128;                     // tokens per macro tile
-constexpr int kXW = 256;                       // weight rows per macro tile (two heads)
-constexpr int kXK = 32;                        // latent columns per stage
-constexpr int kXStages = kLat / kXK;           // 16
+// One GEMM per chunk: [tokens x 512] x [512 x (H x 256)], the latent rows
+// gathered through the block table.  Each workgroup owns one column tile -- the
+// 128 outputs of one head and one product (k^N with W_UK as C[n][t], v with W_UV
+// as C[t][v]) -- and keeps that tile's weights in registers for the whole launch:
+// eight waves, each holding 32 weight rows x 512 latent columns as MFMA fragments
+// (128 VGPRs).  The workgroup then streams its token tiles: stages of 128 latent
+// rows x 128 columns (32 KiB) fill a three-stage LDS ring with direct-to-LDS
+// loads, two stages in flight, one barrier per stage of 32 MFMAs per wave.  The
+// latent is thus the only operand loaded per token tile: 128 KiB for 16.8 MFLOP
+// (128 FLOP per byte, 32 B/clk per CU at the matrix pipe's full rate, under the
+// ~54 B/clk a CU's direct-to-LDS loads sustain).  Wave w covers weight rows
+// 32 (w % 4) .. +32 and tokens 64 (w / 4) .. +64 of a tile.  A finished token tile
+// leaves through an LDS staging area in whole 256-byte rows with non-temporal
+// stores; the k workgroups also copy the tile's RoPE keys, brought into LDS with
+// direct-to-LDS loads along with the stages.  One workgroup per CU; with fewer
+// column tiles than CUs (H < 128) a column tile's token tiles are split among
+// several workgroups.
+constexpr int kXThreads = 512;                 // eight waves
+constexpr int kXWaves = kXThreads / 64;
+constexpr int kXTok = 128;                     // tokens per token tile
+constexpr int kXK = 128;                       // latent columns per stage
+constexpr int kXStagesPerTile = kLat / kXK;    // 4
 constexpr int kXBufs = 3;                      // ring depth
-constexpr int kXThreads = 256;                 // four waves
-constexpr int kXBufBytes = (kXTok + kXW) * kXK * 2;   // 24 KiB
-constexpr int kXLoads = kXBufBytes / 1024 / (kXThreads / 64);   // 6 one-KiB loads per wave per stage
-static_assert(kXLoads * 1024 * (kXThreads / 64) == kXBufBytes, "");
-static_assert(2 * 128 * 272 <= kXBufs * kXBufBytes, "the staged output tile fits in the ring");
-// Operand row r of a stage (64 bytes): granule j stored at j ^ xp_swz(r).  The
-// fragment read (lane (g, q): granule g of row 16 i + q) runs at the LDS's full
-// rate with this map; the map j ^ ((r >> 2) & 3), which spreads 16 rows over 16
-// 16-byte bank groups, ran at 57% of it (timed over all 256 linear maps of the
-// row's low 4 bits to 2 bits; several reach the full rate).
-__device__ __forceinline__ int xp_swz(int r) { return ((r >> 2) & 1) | ((((r >> 1) ^ (r >> 2)) & 1) << 1); }
-__device__ __forceinline__ int xp_off(int r, int j) { return r * 64 + ((j ^ xp_swz(r)) << 4); }
+constexpr int kXStageBytes = kXTok * kXK * 2;  // 32 KiB
+constexpr int kXLoads = kXStageBytes / 1024 / kXWaves;   // 4 one-KiB loads per wave per stage
+constexpr int kXRopeBytes = kXTok * kRope * 2;           // 16 KiB of RoPE keys per token tile
+constexpr int kXRopeLoads = kXRopeBytes / 1024 / kXWaves;   // 2 per wave
+constexpr int kXRowPad = 272;                  // staged output rows: 256 bytes + 16
+constexpr int kXStgOff = kXBufs * kXStageBytes;
+constexpr int kXRopeOff = kXStgOff + 128 * kXRowPad;
+constexpr int kXLdsBytes = kXRopeOff + kXRopeBytes;      // 146 KiB
+static_assert(kXLoads * 1024 * kXWaves == kXStageBytes && kXRopeLoads * 1024 * kXWaves == kXRopeBytes, "");
+static_assert(kXLdsBytes <= 160 * 1024, "LDS");
+
+// Stage row r (one token, 256 bytes = 16 granules): granule j is stored at
+// j ^ (r & 15), so the 16 rows of a fragment read (lane (g, q): granule 4 ks + g of
+// row 16 i + q) fall in 16 different granule columns.
+__device__ __forceinline__ int xs_off(int r, int j) { return r * (kXK * 2) + ((j ^ (r & 15)) << 4); }
 
 // One 16-byte direct-to-LDS load per lane from a per-lane 64-bit address: lane i
 // writes LDS[m0 + 16 i].  The wait states cover M0 written from a VALU-produced
@@ -101,200 +120,236 @@ __device__ __forceinline__ void dma16_v(const void* gaddr, uint32_t lds_addr) {
 // s_waitcnt immediate for "vector memory counter <= n", other counters untouched.
 #define XVMCNT(n) ((((n) & 15) | (((n) >> 4) << 14)) | (7 << 4) | (15 << 8))
 
-// Workgroup (token tile tt, column tile ct): ct < HP forms k^N of heads 2ct, 2ct + 1
-// as C[n][t] (A = W_UK rows, B = latent rows); ct >= HP forms v of heads
-// 2(ct - HP), +1 as C[t][v] (A = latent rows, B = W_UV rows).  HP = ceil(H / 2).
-// A stage holds the A tile first, then the B tile.
-__global__ __launch_bounds__(kXThreads, 2) void mla_expand_kv_kernel(const uint16_t* __restrict__ cache,
+// Vector-memory operations this wave has issued after stage s's loads when it
+// waits for them at the top of iteration s (sl = s % 4; the loads of stage s + 1
+// went out at iteration s - 1; the RoPE keys of tile i go out right after stage
+// 4 i + 2; a tile's output stores go out at the end of its last stage).
+template <bool kIsK>
+constexpr int x_younger(int sl, bool after_tile) {
+  return kXLoads + (kIsK && sl == 2 ? kXRopeLoads : 0) + (kIsK && sl == 1 ? kXRopeLoads : 0) +
+         (after_tile && (sl == 0 || sl == 1) ? (kIsK ? 6 : 4) : 0);
+}
+// s_waitcnt takes an immediate: the counts above, spelled out (the argument is a
+// constant after unrolling, so the switch folds away).
+__device__ __forceinline__ void x_wait(int n) {
+  switch (n) {
+    case 4: __builtin_amdgcn_s_waitcnt(XVMCNT(4)); break;
+    case 6: __builtin_amdgcn_s_waitcnt(XVMCNT(6)); break;
+    case 8: __builtin_amdgcn_s_waitcnt(XVMCNT(8)); break;
+    case 10: __builtin_amdgcn_s_waitcnt(XVMCNT(10)); break;
+    case 12: __builtin_amdgcn_s_waitcnt(XVMCNT(12)); break;
+    default: __builtin_amdgcn_s_waitcnt(XVMCNT(0)); break;
+  }
+}
+
+template <bool kIsK>
+__device__ __forceinline__ void expand_tiles(const uint16_t* __restrict__ cache, const int32_t* __restrict__ block_table,
+                                             int t0, int ntok, int ld, int num_pages, const uint16_t* __restrict__ w,
+                                             uint16_t* __restrict__ out, int h, int tt_begin, int tt_end,
+                                             char* smem) {
+  char LDS_AS* lds = (char LDS_AS*)smem;
+  const uint32_t lds_addr = (uint32_t)(uintptr_t)smem;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, r = lane & 15;
+  const int mo = 32 * (wave & 3);   // this wave's weight rows (outputs)
+  const int tb = 64 * (wave >> 2);  // this wave's tokens within a tile
+
+  // Weights: wf[m][k] = rows mo + 16 m + r of the head's 128, columns 32 k + 8 g .. +8.
+  bf16x8_t wf[2][kLat / 32];
+  {
+    const uint16_t* wr = w + ((size_t)h * 128 + mo + r) * kLat + 8 * g;
+#pragma unroll
+    for (int m = 0; m < 2; m++)
+#pragma unroll
+      for (int k = 0; k < kLat / 32; k++)
+        wf[m][k] = *reinterpret_cast<const bf16x8_t*>(wr + (size_t)16 * m * kLat + 32 * k);
+  }
+  __builtin_amdgcn_s_waitcnt(XVMCNT(0));   // the weights are in before the loads are counted by hand
+
+  // Source rows of this lane's loads for one token tile, as cache row indices
+  // (page * 64 + slot; the byte address is formed at each issue).  Stage load i
+  // fills LDS block 8 i + wave: row 4 (8 i + wave) + lane / 16, physical granule
+  // lane % 16, which holds logical granule (lane % 16) ^ (row & 15).  RoPE load i
+  // fills block 8 i + wave of the RoPE area: token 8 (8 i + wave) + lane / 8,
+  // granule lane % 8.  The tile's tokens lie on at most three pages, read through
+  // the scalar cache.
+  int ridx[kXLoads];
+  int rridx[kXRopeLoads];
+  auto set_rows = [&](int tt) {
+    const int tile_t = tt * kXTok;
+    const int pos_lo = t0 + tile_t;
+    const int pos_hi = t0 + (tile_t + kXTok < ntok ? tile_t + kXTok : ntok) - 1;
+    const int pg_lo = __builtin_amdgcn_readfirstlane(pos_lo / kPage);
+    const int pg_hi = __builtin_amdgcn_readfirstlane(pos_hi / kPage);
+    const int32_t CONST_AS* btc = (const int32_t CONST_AS*)block_table;
+    auto page_at = [&](int u) {   // uniform: a scalar load
+      const int pg = btc[pg_lo + u <= pg_hi ? pg_lo + u : pg_hi];
+      return (pg < 0 || pg >= num_pages) ? 0 : pg;
+    };
+    const int p0 = page_at(0), p1 = page_at(1), p2 = page_at(2);
+    auto row_index = [&](int row) {   // cache row of token tile_t + row (rows past the range repeat the last token)
+      const int t = tile_t + row < ntok ? tile_t + row : ntok - 1;
+      const int pos = t0 + t;
+      const int d = pos / kPage - pg_lo;
+      // Bit masks rather than a chain of selects, which the optimiser turns into a
+      // lookup table in scratch memory.
+      const int m0 = -(int)(d == 0), m1 = -(int)(d == 1);
+      const int pg = (p0 & m0) | (p1 & m1) | (p2 & ~(m0 | m1));
+      return pg * kPage + pos % kPage;
+    };
+    const int l = opaque_lane();
+#pragma unroll
+    for (int i = 0; i < kXLoads; i++) ridx[i] = row_index(4 * (kXWaves * i + wave) + (l >> 4));
+    if (kIsK) {
+#pragma unroll
+      for (int i = 0; i < kXRopeLoads; i++) rridx[i] = row_index(8 * (kXWaves * i + wave) + (l >> 3));
+    }
+  };
+  const char* cache_b = reinterpret_cast<const char*>(cache);
+  auto issue = [&](int buf, int sl) {   // stage sl of the tile set_rows last took, into ring buffer buf
+    const uint32_t base = lds_addr + buf * kXStageBytes;
+    const int l = opaque_lane();
+#pragma unroll
+    for (int i = 0; i < kXLoads; i++) {
+      const int row = 4 * (kXWaves * i + wave) + (l >> 4);
+      const int gb = (((l & 15) ^ (row & 15)) << 4) + sl * kXK * 2;
+      dma16_v(cache_b + (size_t)ridx[i] * (kCacheRow * 2) + gb, base + (kXWaves * i + wave) * 1024);
+    }
+  };
+  auto issue_rope = [&]() {
+    const int l = opaque_lane();
+#pragma unroll
+    for (int i = 0; i < kXRopeLoads; i++)
+      dma16_v(cache_b + (size_t)rridx[i] * (kCacheRow * 2) + kLat * 2 + ((l & 7) << 4),
+              lds_addr + kXRopeOff + (kXWaves * i + wave) * 1024);
+  };
+
+  f32x4_t acc[2][4];   // [weight-row tile][token tile] (k: C[n][t]; v: C[t][v] with the roles swapped)
+#pragma unroll
+  for (int m = 0; m < 2; m++)
+#pragma unroll
+    for (int j = 0; j < 4; j++) acc[m][j] = f32x4_t{};
+
+  const int ntiles = tt_end - tt_begin;
+  const int nst = ntiles * kXStagesPerTile;
+  if (ntiles <= 0) return;
+  set_rows(tt_begin);
+  issue(0, 0);
+  issue(1, 1);
+  for (int ti = 0; ti < ntiles; ti++) {
+    const int tile_t = (tt_begin + ti) * kXTok;
+#pragma unroll
+    for (int sl = 0; sl < kXStagesPerTile; sl++) {
+      const int s = ti * kXStagesPerTile + sl;
+      // Wait for this wave's loads of stage s; later ones may stay in flight.
+      if (s + 1 >= nst) __builtin_amdgcn_s_waitcnt(XVMCNT(0));
+      else if (ti > 0) x_wait(x_younger<kIsK>(sl, true));
+      else x_wait(x_younger<kIsK>(sl, false));
+      __syncthreads();   // stage s is in LDS for every wave; buffer (s + 2) % 3 is free
+      if (s + 2 < nst) {
+        if (sl == 2) set_rows(tt_begin + ti + 1);   // stage s + 2 opens the next tile
+        issue((s + 2) % kXBufs, (sl + 2) % kXStagesPerTile);
+        if (kIsK && sl == 0) issue_rope();          // this tile's RoPE keys, after stage 4 ti + 2
+      }
+      const char LDS_AS* base = lds + (s % kXBufs) * kXStageBytes;
+      bf16x8_t lf[4], ln[4];
+#pragma unroll
+      for (int j = 0; j < 4; j++) lf[j] = lds_b128(base + xs_off(tb + 16 * j + r, g));
+#pragma unroll
+      for (int ks = 0; ks < kXK / 32; ks++) {
+        if (ks + 1 < kXK / 32) {
+#pragma unroll
+          for (int j = 0; j < 4; j++) ln[j] = lds_b128(base + xs_off(tb + 16 * j + r, 4 * (ks + 1) + g));
+        }
+        const int kg = sl * (kXK / 32) + ks;
+#pragma unroll
+        for (int m = 0; m < 2; m++)
+#pragma unroll
+          for (int j = 0; j < 4; j++)
+            acc[m][j] = kIsK ? __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[m][kg], lf[j], acc[m][j], 0, 0, 0)
+                             : __builtin_amdgcn_mfma_f32_16x16x32_bf16(lf[j], wf[m][kg], acc[m][j], 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < 4; j++) lf[j] = ln[j];
+        __builtin_amdgcn_sched_barrier(0);   // keep the next K-step's reads ahead of these MFMAs
+      }
+    }
+
+    // Epilogue of the tile.  Lane (g, r) holds, for k, C[n = mo + 16 m + 4 g + e][t = tb + 16 j + r]
+    // and, for v, C[t = tb + 16 j + 4 g + e][v = mo + 16 m + r].  The staged tile is
+    // [row][128 values] in bf16 with 272-byte rows: k rows are tokens (values: the
+    // head's 128 outputs), v rows are dims (values: the tile's 128 tokens).  Tokens
+    // past the range are written as zeros.  (The staging area was last read four
+    // barriers ago.)
+    char LDS_AS* stg = lds + kXStgOff;
+#pragma unroll
+    for (int m = 0; m < 2; m++)
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        bf16x4_t v4;
+        if (kIsK) {
+          const int tl = tb + 16 * j + r;
+          const bool live = tile_t + tl < ntok;
+#pragma unroll
+          for (int e = 0; e < 4; e++) v4[e] = live ? (__bf16)acc[m][j][e] : (__bf16)0.f;
+          *reinterpret_cast<bf16x4_t LDS_AS*>(stg + tl * kXRowPad + (mo + 16 * m + 4 * g) * 2) = v4;
+        } else {
+          const int tl = tb + 16 * j + 4 * g;
+#pragma unroll
+          for (int e = 0; e < 4; e++) v4[e] = tile_t + tl + e < ntok ? (__bf16)acc[m][j][e] : (__bf16)0.f;
+          *reinterpret_cast<bf16x4_t LDS_AS*>(stg + (mo + 16 * m + r) * kXRowPad + tl * 2) = v4;
+        }
+        acc[m][j] = f32x4_t{};
+      }
+    __syncthreads();   // staged tile complete; the RoPE keys landed before this stage's barrier
+    // 128 rows x 16 granules: four per thread, sixteen consecutive lanes per row.
+    // Non-temporal: the expanded chunk is far larger than the caches.
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      const int x = tid + u * kXThreads;
+      const int gr = x & 15, row = x >> 4;
+      const i32x4_t v = *reinterpret_cast<const i32x4_t LDS_AS*>(stg + row * kXRowPad + gr * 16);
+      if (kIsK) {
+        const int t = tile_t + row;
+        if (t < ld) __builtin_nontemporal_store(v, reinterpret_cast<i32x4_t*>(out + ((size_t)h * ld + t) * kQK + 8 * gr));
+      } else {
+        const int t = tile_t + 8 * gr;   // ld is a multiple of 64: t < ld covers the granule
+        if (t < ld) __builtin_nontemporal_store(v, reinterpret_cast<i32x4_t*>(out + ((size_t)h * kDv + row) * ld + t));
+      }
+    }
+    if (kIsK) {
+      // k^R: k[h][t][128 .. 191] = the cached RoPE key of token t (zeros past the range).
+#pragma unroll
+      for (int u = 0; u < 2; u++) {
+        const int x = tid + u * kXThreads;
+        const int part = x & 7, tok = x >> 3;
+        const int t = tile_t + tok;
+        i32x4_t v = *reinterpret_cast<const i32x4_t LDS_AS*>(lds + kXRopeOff + tok * (kRope * 2) + part * 16);
+        if (t >= ntok) v = i32x4_t{};
+        if (t < ld)
+          __builtin_nontemporal_store(v, reinterpret_cast<i32x4_t*>(out + ((size_t)h * ld + t) * kQK + kNope + 8 * part));
+      }
+    }
+  }
+}
+
+// Workgroup i: column tile ct = i / nsp (ct < H: k^N of head ct; else v of head
+// ct - H), token tiles [sp ntt / nsp, (sp + 1) ntt / nsp) with sp = i % nsp.
+__global__ __launch_bounds__(kXThreads, 1) void mla_expand_kv_kernel(const uint16_t* __restrict__ cache,
                                                                     const int32_t* __restrict__ block_table, int t0,
                                                                     int ntok, int ld, int num_pages,
                                                                     const uint16_t* __restrict__ w_uk,
                                                                     const uint16_t* __restrict__ w_uv,
                                                                     uint16_t* __restrict__ k_out,
-                                                                    uint16_t* __restrict__ vt_out, int H, int ntt) {
-  __shared__ __attribute__((aligned(1024))) char smem[kXBufs * kXBufBytes];
-  char LDS_AS* lds = (char LDS_AS*)smem;
-  const uint32_t lds_addr = (uint32_t)(uintptr_t)smem;
-  const int HP = (H + 1) / 2;
-  // blockIdx -> tiles.  Workgroups are dealt to the 8 XCDs round robin; when the
-  // counts allow, XCD x gets token tiles [x ntt/8, (x+1) ntt/8) of every column
-  // tile, column tiles outermost, so its L2 holds those latent rows for the whole
-  // launch and the weight tiles of the column tiles in progress.
-  int tt, ct;
-  {
-    const int nblk = gridDim.x;
-    const int lin = blockIdx.x;
-    if ((ntt & 7) == 0 && (nblk & 7) == 0) {
-      const int per = ntt >> 3, idx = lin >> 3;
-      tt = (lin & 7) * per + idx % per;
-      ct = idx / per;
-    } else {
-      tt = lin % ntt;
-      ct = lin / ntt;
-    }
-  }
-  const bool is_k = ct < HP;
-  const int hp = is_k ? ct : ct - HP;
-  const int tile_t = tt * kXTok;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g = lane >> 4, r = lane & 15;
-  // 1-KiB blocks of a stage: k: weights 0..15, latent 16..23; v: latent 0..7, weights 8..23.
-  const int lat_blk0 = is_k ? kXW / 16 : 0;
-  const int w_blk0 = is_k ? 0 : kXTok / 16;
-
-  // Per-lane source rows of this wave's six loads of a stage: load i is block
-  // b = 4 i + wave; lane granule G = 64 (b - first block of its tile) + lane is
-  // row G / 4 of that tile, stored granule G % 4, which holds logical granule
-  // (G % 4) ^ xp_swz(row).
-  const uint16_t* wt = (is_k ? w_uk : w_uv);
-  // The tile's tokens lie on at most three pages: their block-table entries are
-  // read once through the scalar cache (uniform loads), not once per lane.
-  const int pos_lo = t0 + tile_t;
-  const int pos_hi = t0 + (tile_t + kXTok - 1 < ntok - 1 ? tile_t + kXTok - 1 : ntok - 1);
-  const int pg_lo = __builtin_amdgcn_readfirstlane(pos_lo / kPage);
-  const int pg_hi = __builtin_amdgcn_readfirstlane(pos_hi / kPage);
-  const int32_t CONST_AS* btc = (const int32_t CONST_AS*)block_table;
-  int pages3[3];
-#pragma unroll
-  for (int u = 0; u < 3; u++) {
-    int pg = btc[pg_lo + u <= pg_hi ? pg_lo + u : pg_hi];
-    pages3[u] = (pg < 0 || pg >= num_pages) ? 0 : pg;
-  }
-  auto page_of = [&](int pos) {   // pos within [pos_lo, pos_hi]
-    const int d = pos / kPage - pg_lo;
-    return d == 0 ? pages3[0] : (d == 1 ? pages3[1] : pages3[2]);
-  };
-  const char* src[kXLoads];
-#pragma unroll
-  for (int i = 0; i < kXLoads; i++) {
-    const int b = 4 * i + wave;
-    const bool latent = is_k ? b >= lat_blk0 : b < w_blk0;
-    const int G = 64 * (b - (latent ? lat_blk0 : w_blk0)) + lane;
-    const int row = G >> 2;
-    const int j = (G & 3) ^ xp_swz(row);
-    const uint16_t* p;
-    if (latent) {
-      int t = tile_t + row;
-      t = t < ntok ? t : ntok - 1;
-      const int pos = t0 + t;
-      p = cache + ((size_t)page_of(pos) * kPage + pos % kPage) * kCacheRow;
-    } else {
-      int h = 2 * hp + (row >> 7);
-      h = h < H ? h : H - 1;
-      p = wt + ((size_t)h * kNope + (row & 127)) * kLat;
-    }
-    src[i] = reinterpret_cast<const char*>(p) + 16 * j;
-  }
-  __builtin_amdgcn_s_waitcnt(XVMCNT(0));   // block-table reads done before the loads are counted by hand
-
-  auto issue = [&](int st) {
-    const uint32_t base = lds_addr + (st % kXBufs) * kXBufBytes;
-#pragma unroll
-    for (int i = 0; i < kXLoads; i++) dma16_v(src[i] + st * kXK * 2, base + (4 * i + wave) * 1024);
-  };
-
-  // This wave's part: A rows abase + 16 i + r (i < 8), B rows bbase + 16 j + r (j < 4).
-  const int abase = is_k ? 128 * (wave & 1) : 0;
-  const int bbase = is_k ? 64 * (wave >> 1) : 64 * wave;
-  const int b_off = (is_k ? kXW : kXTok) * kXK * 2;   // the B tile's byte offset in a stage
-  f32x4_t acc[8][4];
-#pragma unroll
-  for (int i = 0; i < 8; i++)
-#pragma unroll
-    for (int j = 0; j < 4; j++) acc[i][j] = f32x4_t{};
-
-  issue(0);
-  issue(1);
-  for (int st = 0; st < kXStages; st++) {
-    if (st + 1 < kXStages) __builtin_amdgcn_s_waitcnt(XVMCNT(kXLoads));   // stage st + 1 may stay in flight
-    else __builtin_amdgcn_s_waitcnt(XVMCNT(0));
-    __syncthreads();   // every wave's loads of stage st have landed; buffer (st - 1) % 3 is free
-    if (st + 2 < kXStages) issue(st + 2);
-    const char LDS_AS* base = lds + (st % kXBufs) * kXBufBytes;
-    bf16x8_t af[8], bfr[4];
-#pragma unroll
-    for (int i = 0; i < 8; i++) af[i] = lds_b128(base + xp_off(abase + 16 * i + r, g));
-#pragma unroll
-    for (int j = 0; j < 4; j++) bfr[j] = lds_b128(base + b_off + xp_off(bbase + 16 * j + r, g));
-#pragma unroll
-    for (int i = 0; i < 8; i++)
-#pragma unroll
-      for (int j = 0; j < 4; j++) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-  }
-
-  // Epilogue through LDS, so that global stores are whole 256-byte rows: lane (g, r)
-  // holds C[abase + 16 i + 4 g + e][bbase + 16 j + r], e = 0..3.  The staged tile
-  // is [head][row][128 values] in bf16 with rows padded to 272 bytes (16 lanes of
-  // a store land in 16 bank groups): k^N rows are tokens (values = the head's 128
-  // outputs), v rows are the head's 128 dims (values = the tile's 128 tokens).
-  // Tokens past the range are written as zeros.
-  constexpr int kRowPad = 272;
-  __syncthreads();   // every wave is done with the ring
-  char LDS_AS* stg = lds;
-  if (is_k) {
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const int tl = bbase + 16 * j + r;   // token within the tile
-      const bool live = tile_t + tl < ntok;
-#pragma unroll
-      for (int i = 0; i < 8; i++) {
-        const int m = abase + 16 * i + 4 * g;
-        bf16x4_t w;
-#pragma unroll
-        for (int e = 0; e < 4; e++) w[e] = live ? (__bf16)acc[i][j][e] : (__bf16)0.f;
-        *reinterpret_cast<bf16x4_t LDS_AS*>(stg + ((m >> 7) * kXTok + tl) * kRowPad + (m & 127) * 2) = w;
-      }
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-      const int tl = 16 * i + 4 * g;   // first of four tokens within the tile
-#pragma unroll
-      for (int j = 0; j < 4; j++) {
-        const int n = bbase + 16 * j + r;
-        bf16x4_t w;
-#pragma unroll
-        for (int e = 0; e < 4; e++) w[e] = tile_t + tl + e < ntok ? (__bf16)acc[i][j][e] : (__bf16)0.f;
-        *reinterpret_cast<bf16x4_t LDS_AS*>(stg + ((n >> 7) * kDv + (n & 127)) * kRowPad + tl * 2) = w;
-      }
-    }
-  }
-  __syncthreads();
-  // 2 heads x 128 rows x 16 granules: 16 per thread, 16 consecutive lanes per row.
-#pragma unroll 4
-  for (int x = tid; x < 2 * 128 * 16; x += kXThreads) {
-    const int gr = x & 15, row = (x >> 4) & 127, hh = x >> 11;
-    const int h = 2 * hp + hh;
-    if (h >= H) continue;
-    const bf16x8_t v = *reinterpret_cast<const bf16x8_t LDS_AS*>(stg + (hh * 128 + row) * kRowPad + gr * 16);
-    // Non-temporal: the expanded chunk is far larger than the caches (measured: the
-    // kernel 21% faster than with ordinary stores).
-    const i32x4_t vi = __builtin_bit_cast(i32x4_t, v);
-    if (is_k) {
-      const int t = tile_t + row;
-      if (t < ld) __builtin_nontemporal_store(vi, reinterpret_cast<i32x4_t*>(k_out + ((size_t)h * ld + t) * kQK + 8 * gr));
-    } else {
-      const int t = tile_t + 8 * gr;   // ld is a multiple of 64: t < ld covers the granule
-      if (t < ld) __builtin_nontemporal_store(vi, reinterpret_cast<i32x4_t*>(vt_out + ((size_t)h * kDv + row) * ld + t));
-    }
-  }
-  if (is_k) {
-    // k^R: k[h][t][128 .. 191] = the cached RoPE key of token t (zeros past the range).
-    for (int x = tid; x < kXTok * 2 * (kRope / 8); x += kXThreads) {
-      const int part = x & 7, hh = (x >> 3) & 1, jt = x >> 4;
-      const int t = tile_t + jt, h = 2 * hp + hh;
-      if (t >= ld || h >= H) continue;
-      bf16x8_t v = bf16x8_t{};
-      if (t < ntok) {
-        const int pos = t0 + t;
-        v = *reinterpret_cast<const bf16x8_t*>(cache + ((size_t)page_of(pos) * kPage + pos % kPage) * kCacheRow + kLat +
-                                                8 * part);
-      }
-      __builtin_nontemporal_store(__builtin_bit_cast(i32x4_t, v),
-                                  reinterpret_cast<i32x4_t*>(k_out + ((size_t)h * ld + t) * kQK + kNope + 8 * part));
-    }
-  }
+                                                                    uint16_t* __restrict__ vt_out, int H, int ntt,
+                                                                    int nsp) {
+  __shared__ __attribute__((aligned(1024))) char smem[kXLdsBytes];
+  const int ct = blockIdx.x / nsp, sp = blockIdx.x % nsp;
+  const int tt_begin = (int)((int64_t)sp * ntt / nsp), tt_end = (int)((int64_t)(sp + 1) * ntt / nsp);
+  if (ct < H)
+    expand_tiles<true>(cache, block_table, t0, ntok, ld, num_pages, w_uk, k_out, ct, tt_begin, tt_end, smem);
+  else
+    expand_tiles<false>(cache, block_table, t0, ntok, ld, num_pages, w_uv, vt_out, ct - H, tt_begin, tt_end, smem);
 }
 
 // ===========================================================================
@@ -541,10 +596,17 @@ hipError_t launch_expand_kv(const uint16_t* cache, const int32_t* block_table, i
                             hipStream_t stream) {
   int ld = (ntok + 63) / 64 * 64;
   int ntt = (ld + kXTok - 1) / kXTok;
-  const int nct = 2 * ((H + 1) / 2);
+  const int nct = 2 * H;
+  // One workgroup per CU: a column tile's token tiles are split among cus / nct workgroups.
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+  int nsp = cus / nct > 1 ? cus / nct : 1;
+  nsp = nsp < ntt ? nsp : ntt;
   void* args[] = {(void*)&cache, (void*)&block_table, (void*)&t0,    (void*)&ntok,   (void*)&ld, (void*)&num_pages,
-                  (void*)&w_uk,  (void*)&w_uv,        (void*)&k_out, (void*)&vt_out, (void*)&H,  (void*)&ntt};
-  return hipLaunchKernel((const void*)mla_expand_kv_kernel, dim3(ntt * nct), dim3(kXThreads), args, 0, stream);
+                  (void*)&w_uk,  (void*)&w_uv,        (void*)&k_out, (void*)&vt_out, (void*)&H,  (void*)&ntt,
+                  (void*)&nsp};
+  return hipLaunchKernel((const void*)mla_expand_kv_kernel, dim3(nct * nsp), dim3(kXThreads), args, 0, stream);
 }
 
 hipError_t launch_prefill_attention(const uint16_t* q, const uint16_t* k, const uint16_t* vt, int t0, int ntok, int n,
