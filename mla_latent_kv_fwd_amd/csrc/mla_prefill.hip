@@ -355,15 +355,18 @@ __global__ __launch_bounds__(kXThreads, 1) void mla_expand_kv_kernel(const uint1
 // ===========================================================================
 // Attention over one expanded chunk
 // ===========================================================================
-constexpr int kAttThreads = 256;
-constexpr int kAttQ = 128;                   // queries per workgroup (4 waves x 32)
+constexpr int kAttThreads = 512;
+constexpr int kAttWaves = kAttThreads / 64;
+constexpr int kAttQ = 32 * kAttWaves;        // queries per workgroup (8 waves x 32)
+constexpr int kAttBufs = 3;                  // LDS ring of key blocks, two in flight
 constexpr int kKBlk = 64;                    // keys per LDS block
 constexpr int kKBytes = kKBlk * kQK * 2;     // 24 KiB: 64 rows x 384 bytes
 constexpr int kVBytes = kDv * kKBlk * 2;     // 16 KiB: 128 dim rows x 128 bytes
 constexpr int kStage = kKBytes + kVBytes;    // 40 KiB
 constexpr int kGranK = kKBlk * (kQK / 8);    // 1,536 granules
 constexpr int kGranV = kDv * (kKBlk / 8);    // 1,024 granules
-static_assert(kGranK % kAttThreads == 0 && kGranV % kAttThreads == 0, "whole granules per thread");
+constexpr int kAttLoads = kStage / 1024 / kAttWaves;   // 5 one-KiB direct-to-LDS loads per wave per block
+static_assert(kAttLoads * 1024 * kAttWaves == kStage && kKBytes % 1024 == 0, "whole one-KiB loads per wave");
 
 // K rows (384 bytes, 24 granules): the low 3 bits of the granule index are XORed
 // with bits (1, 3, 4) of the token, which makes the 16 (permuted) token rows of a
@@ -374,11 +377,12 @@ __device__ __forceinline__ int k_off(int t, int j) {
 }
 __device__ __forceinline__ int v_off(int d, int j) { return kKBytes + d * (kKBlk * 2) + ((j ^ ((d >> 1) & 7)) << 4); }
 
-__global__ __launch_bounds__(kAttThreads, 2) void mla_prefill_attention_kernel(
+__global__ __launch_bounds__(kAttThreads, 1) void mla_prefill_attention_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kbuf, const uint16_t* __restrict__ vtbuf, int t0,
     int ntok, int ld, int n, int L, int H, float scale_log2, float* __restrict__ out, float* __restrict__ lse) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * kStage];
+  __shared__ __attribute__((aligned(1024))) char smem[kAttBufs * kStage];
   char LDS_AS* lds = (char LDS_AS*)smem;
+  const uint32_t lds_addr = (uint32_t)(uintptr_t)smem;
   // blockIdx -> (head, query block).  Workgroups are dealt to the 8 XCDs round robin
   // (linear id % 8); when H is a multiple of 8, head h runs only on XCD h % 8 with
   // all its query blocks together, so a head's K and V stay in that XCD's L2.
@@ -393,7 +397,8 @@ __global__ __launch_bounds__(kAttThreads, 2) void mla_prefill_attention_kernel(
     h = 8 * hh + (lin & 7);
   }
   const int qb = (nqb - 1 - qbi) * kAttQ;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, r = lane & 15;
 
   // Key blocks this workgroup needs: positions up to its last query's.
@@ -420,35 +425,36 @@ __global__ __launch_bounds__(kAttThreads, 2) void mla_prefill_attention_kernel(
     }
   }
 
-  // Block loads: K granules gi = tid + 256 u (u < 6), V^T granules x = tid + 256 u (u < 4).
+  // Key blocks stream HBM -> LDS with direct-to-LDS loads into a three-block ring.
+  // One-KiB LDS block b of a ring slot (b < 24: K, else V^T) is loaded by wave
+  // b % 8 as its load b / 8; lane l of it fills K granule gi = 64 b + l (row
+  // t = gi / 24, physical granule gi % 24) or V^T granule x = 64 (b - 24) + l (row
+  // d = x / 8, physical granule x % 8), so each lane reads the logical granule the
+  // swizzle puts there.  Source offsets (elements, within the head's K or V^T) are
+  // per lane and fixed; block kb adds kb * 64 rows of K or kb * 64 columns of V^T.
   const uint16_t* kh = kbuf + (size_t)h * ld * kQK;
   const uint16_t* vh = vtbuf + (size_t)h * kDv * ld;
-  constexpr int kUK = kGranK / kAttThreads, kUV = kGranV / kAttThreads;   // 6, 4
-  bf16x8_t pre[kUK + kUV];
-  auto fetch = [&](int kb) {
+  int soff[kAttLoads];
 #pragma unroll
-    for (int u = 0; u < kUK; u++) {
-      const int gi = tid + u * kAttThreads;
-      const int t = gi / (kQK / 8), j = gi % (kQK / 8);
-      pre[u] = *reinterpret_cast<const bf16x8_t*>(kh + (size_t)(kb * kKBlk + t) * kQK + 8 * j);
+  for (int i = 0; i < kAttLoads; i++) {
+    const int b = kAttWaves * i + wave;
+    if (b < kKBytes / 1024) {
+      const int gi = 64 * b + lane, t = gi / (kQK / 8), p = gi % (kQK / 8);
+      const int sw = ((t >> 1) & 1) | ((t >> 2) & 6);
+      const int j = (p & ~7) | ((p & 7) ^ sw);
+      soff[i] = t * kQK + 8 * j;
+    } else {
+      const int x = 64 * (b - kKBytes / 1024) + lane, d = x >> 3, jp = x & 7;
+      soff[i] = d * ld + 8 * (jp ^ ((d >> 1) & 7));
     }
+  }
+  auto issue = [&](int kb) {
+    const uint32_t base = lds_addr + (kb % kAttBufs) * kStage;
 #pragma unroll
-    for (int u = 0; u < kUV; u++) {
-      const int x = tid + u * kAttThreads, d = x >> 3, j = x & 7;
-      pre[kUK + u] = *reinterpret_cast<const bf16x8_t*>(vh + (size_t)d * ld + kb * kKBlk + 8 * j);
-    }
-  };
-  auto stash = [&](int buf) {
-    char LDS_AS* base = lds + buf * kStage;
-#pragma unroll
-    for (int u = 0; u < kUK; u++) {
-      const int gi = tid + u * kAttThreads;
-      lds_w128(base + k_off(gi / (kQK / 8), gi % (kQK / 8)), pre[u]);
-    }
-#pragma unroll
-    for (int u = 0; u < kUV; u++) {
-      const int x = tid + u * kAttThreads;
-      lds_w128(base + v_off(x >> 3, x & 7), pre[kUK + u]);
+    for (int i = 0; i < kAttLoads; i++) {
+      const int b = kAttWaves * i + wave;
+      const uint16_t* src = b < kKBytes / 1024 ? kh + (size_t)kb * kKBlk * kQK + soff[i] : vh + kb * kKBlk + soff[i];
+      dma16_v(src, base + b * 1024);
     }
   };
 
@@ -463,14 +469,17 @@ __global__ __launch_bounds__(kAttThreads, 2) void mla_prefill_attention_kernel(
   // Score-tile row m of tile a is token 8(m/4) + m%4 of the 32-token group; tile b adds 4.
   const int ta = 8 * (r >> 2) + (r & 3);
 
-  if (nblk > 0) {
-    fetch(0);
-    stash(0);
-  }
-  __syncthreads();
+  // The queries were loaded by the compiler; they are in before the loads are counted by hand.
+  __builtin_amdgcn_s_waitcnt(XVMCNT(0));
+  if (nblk > 0) issue(0);
+  if (nblk > 1) issue(1);
   for (int kb = 0; kb < nblk; kb++) {
-    if (kb + 1 < nblk) fetch(kb + 1);
-    const char LDS_AS* base = lds + (kb & 1) * kStage;
+    // This wave's loads of block kb have landed (block kb + 1's may still be in flight).
+    if (kb + 1 < nblk) __builtin_amdgcn_s_waitcnt(XVMCNT(kAttLoads));
+    else __builtin_amdgcn_s_waitcnt(XVMCNT(0));
+    __syncthreads();   // block kb is in LDS for every wave; slot (kb + 2) % 3 is free
+    if (kb + 2 < nblk) issue(kb + 2);
+    const char LDS_AS* base = lds + (kb % kAttBufs) * kStage;
     const int kpos0 = t0 + kb * kKBlk;   // position of the block's first key
     const bool need_mask = (kb * kKBlk + kKBlk > ntok) || (kpos0 + kKBlk - 1 > pos_first);
 #pragma unroll
@@ -534,8 +543,6 @@ __global__ __launch_bounds__(kAttThreads, 2) void mla_prefill_attention_kernel(
         for (int qt = 0; qt < 2; qt++) o[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[qt], o[qt][dt], 0, 0, 0);
       }
     }
-    if (kb + 1 < nblk) stash((kb + 1) & 1);   // that buffer was last read in block kb-1
-    __syncthreads();
   }
 
   // Finalise: lane (g, r) holds O^T[16 dt + 4g + e][query qw + 16 qt + r].
