@@ -76,7 +76,8 @@ def _latents(pw):
 
 # ------------------------------------------------------------------ expansion
 @pytest.mark.parametrize("H,L,t0,ntok", [(16, 700, 0, 700), (128, 300, 64, 200), (4, 5000, 1000, 4000),
-                                         (8, 130, 129, 1), (3, 1000, 100, 777), (1, 64, 0, 64), (127, 600, 37, 300)])
+                                         (8, 130, 129, 1), (3, 1000, 100, 777), (1, 64, 0, 64), (127, 600, 37, 300),
+                                         (64, 3300, 250, 3000), (128, 2200, 0, 2200)])
 def test_expand_kv_matches_oracle(torch, M, H, L, t0, ntok):
     pw = W.make_prefill_workload("exp", num_heads=H, num_new=1, seqlen=L, seed=H + L + t0)
     _say(f"expand_kv H={H} L={L} t0={t0} ntok={ntok}")
@@ -133,7 +134,7 @@ def _check_rows(got_o, got_l, ref_o, ref_l, what, lse_bound=None):
 
 @pytest.mark.parametrize("H,n,L,t0,ntok", [(16, 200, 1000, 0, 1000), (16, 130, 1000, 640, 360),
                                            (8, 100, 1000, 950, 50), (128, 64, 64, 0, 64), (4, 300, 5000, 1024, 1500),
-                                           (2, 1, 77, 0, 77)])
+                                           (2, 1, 77, 0, 77), (8, 600, 2000, 1400, 600), (16, 520, 1800, 0, 1800)])
 def test_prefill_attention_matches_oracle(torch, M, H, n, L, t0, ntok):
     rng = np.random.default_rng(H * 1000 + n + t0)
     q = W.f32_to_bf16_bits(rng.standard_normal((n, H, 192), dtype=np.float32))
