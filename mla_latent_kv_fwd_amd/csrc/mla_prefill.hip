@@ -363,8 +363,6 @@ constexpr int kKBlk = 64;                    // keys per LDS block
 constexpr int kKBytes = kKBlk * kQK * 2;     // 24 KiB: 64 rows x 384 bytes
 constexpr int kVBytes = kDv * kKBlk * 2;     // 16 KiB: 128 dim rows x 128 bytes
 constexpr int kStage = kKBytes + kVBytes;    // 40 KiB
-constexpr int kGranK = kKBlk * (kQK / 8);    // 1,536 granules
-constexpr int kGranV = kDv * (kKBlk / 8);    // 1,024 granules
 constexpr int kAttLoads = kStage / 1024 / kAttWaves;   // 5 one-KiB direct-to-LDS loads per wave per block
 static_assert(kAttLoads * 1024 * kAttWaves == kStage && kKBytes % 1024 == 0, "whole one-KiB loads per wave");
 
