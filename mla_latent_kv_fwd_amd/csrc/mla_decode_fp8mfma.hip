@@ -539,7 +539,7 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_fp8_mfma_kernel(Decode
         const int slot_id = rq.slot_off + split;
         if (slot_id >= 0 && slot_id < 2 * a.nwg) {
           const size_t pidx = ((size_t)slot_id * a.nrb + rb) * kRowsPerBlock + orow_local;
-          store_partial(a, pidx, oq, o, inv, lse_v);
+          store_partial_direct(a, pidx, oq, o, inv, lse_v);
         }
       }
     }

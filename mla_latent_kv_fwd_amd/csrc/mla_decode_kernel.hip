@@ -384,10 +384,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_bf16_kernel(DecodeArgs
         }
       } else {
         const int slot_id = rq.slot_off + split;
-        if (slot_id >= 0 && slot_id < 2 * a.nwg) {
-          const size_t pidx = ((size_t)slot_id * a.nrb + rb) * kRowsPerBlock + orow_local;
-          store_partial(a, pidx, oq, o, inv, lse_v);
-        }
+        if (slot_id >= 0 && slot_id < 2 * a.nwg)   // uniform
+          store_partial(a, ((size_t)slot_id * a.nrb + rb) * kRowsPerBlock, smem, o, inv, lse_v);
       }
     }
     gpage = rq.page_first + pg1;
@@ -759,10 +757,8 @@ __global__ __launch_bounds__(kThreads, 1) void mla_decode_fp8_kernel(DecodeArgs 
         }
       } else {
         const int slot_id = rq.slot_off + split;
-        if (slot_id >= 0 && slot_id < 2 * a.nwg) {
-          const size_t pidx = ((size_t)slot_id * a.nrb + rb) * kRowsPerBlock + orow_local;
-          store_partial(a, pidx, oq, o, inv, lse_v);
-        }
+        if (slot_id >= 0 && slot_id < 2 * a.nwg)   // uniform
+          store_partial(a, ((size_t)slot_id * a.nrb + rb) * kRowsPerBlock, smem, o, inv, lse_v);
       }
     }
     gpage = rq.page_first + pg1;

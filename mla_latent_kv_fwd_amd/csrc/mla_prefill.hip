@@ -43,7 +43,6 @@ constexpr float kLazyRescale = 8.0f;      // log2 of the largest p kept unrescal
 constexpr float kLn2 = 0.69314718055994531f;
 
 __device__ __forceinline__ bf16x8_t lds_b128(const char LDS_AS* p) { return *reinterpret_cast<const bf16x8_t LDS_AS*>(p); }
-__device__ __forceinline__ void lds_w128(char LDS_AS* p, bf16x8_t v) { *reinterpret_cast<bf16x8_t LDS_AS*>(p) = v; }
 
 // The lane index, hidden from the optimiser: per-lane address terms derived from
 // it are recomputed where they are used rather than kept live across loops.
