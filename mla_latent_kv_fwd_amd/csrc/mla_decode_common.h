@@ -128,11 +128,20 @@ __device__ __forceinline__ void store_partial(const DecodeArgs& a, size_t pbase,
   __syncthreads();
   typedef int i32x4_st __attribute__((ext_vector_type(4)));
   char* pout = a.ws + a.lay.part_out + pbase * (kHeadDimV * 2);
-#pragma unroll 4
-  for (int x = (int)threadIdx.x; x < kRowsPerBlock * (kHeadDimV * 2 / 16); x += kThreads) {
-    const int row = x >> 6, gr = x & 63;
-    const i32x4_st v = *reinterpret_cast<const i32x4_st LDS_AS*>(stage + row * kPitch + gr * 16);
-    *reinterpret_cast<i32x4_st*>(pout + (size_t)row * (kHeadDimV * 2) + gr * 16) = v;
+  // 128 rows x 64 granules over 512 threads: thread x moves granule x & 63 of
+  // rows x / 64 + 8i, i = 0..15, read four at a time so the LDS latency is
+  // paid four times rather than sixteen.
+  static_assert(kRowsPerBlock * (kHeadDimV * 2 / 16) == 16 * kThreads, "");
+  const int x0 = (int)threadIdx.x;
+  const char LDS_AS* src = stage + (x0 >> 6) * kPitch + (x0 & 63) * 16;
+  char* dst = pout + (size_t)(x0 >> 6) * (kHeadDimV * 2) + (x0 & 63) * 16;
+#pragma unroll
+  for (int h = 0; h < 4; h++) {
+    i32x4_st v[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) v[j] = *reinterpret_cast<const i32x4_st LDS_AS*>(src + (4 * h + j) * 8 * kPitch);
+#pragma unroll
+    for (int j = 0; j < 4; j++) *reinterpret_cast<i32x4_st*>(dst + (4 * h + j) * 8 * (kHeadDimV * 2)) = v[j];
   }
 }
 

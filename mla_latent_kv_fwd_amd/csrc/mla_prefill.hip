@@ -9,8 +9,8 @@
 //
 // Expansion is a GEMM [tokens x 512] x [512 x (H x 256)] with the latent rows
 // gathered through the block table: each workgroup keeps one head's weights of
-// one product in registers and streams 128-token tiles of the latent through LDS
-// with direct-to-LDS loads, one workgroup per CU (details at the kernel).
+// one product in registers and streams 64-token tiles of the latent through LDS
+// with direct-to-LDS loads, two workgroups per CU (details at the kernel).
 //
 // Attention keeps the decode kernel's orientation -- scores as S^T = K . q^T,
 // lane = query -- with 32 queries per wave, so every K or V^T fragment read
@@ -72,40 +72,43 @@ __device__ __forceinline__ float row_sum(float x) {
 // gathered through the block table.  Each workgroup owns one column tile -- the
 // 128 outputs of one head and one product (k^N with W_UK as C[n][t], v with W_UV
 // as C[t][v]) -- and keeps that tile's weights in registers for the whole launch:
-// eight waves, each holding 32 weight rows x 512 latent columns as MFMA fragments
-// (128 VGPRs).  The workgroup then streams its token tiles: stages of 128 latent
-// rows x 128 columns (32 KiB) fill a three-stage LDS ring with direct-to-LDS
+// four waves, each holding 32 weight rows x 512 latent columns as MFMA fragments
+// (128 VGPRs).  The workgroup then streams its token tiles: stages of 64 latent
+// rows x 128 columns (16 KiB) fill a three-stage LDS ring with direct-to-LDS
 // loads, two stages in flight, one barrier per stage of 32 MFMAs per wave.  The
-// latent is thus the only operand loaded per token tile: 128 KiB for 16.8 MFLOP
+// latent is thus the only operand loaded per token tile: 64 KiB for 8.4 MFLOP
 // (128 FLOP per byte, 32 B/clk per CU at the matrix pipe's full rate, under the
 // ~54 B/clk a CU's direct-to-LDS loads sustain).  Wave w covers weight rows
-// 32 (w % 4) .. +32 and tokens 64 (w / 4) .. +64 of a tile.  A finished token tile
-// leaves through an LDS staging area in whole 256-byte rows with non-temporal
-// stores; the k workgroups also copy the tile's RoPE keys, brought into LDS with
-// direct-to-LDS loads along with the stages.  One workgroup per CU; with fewer
-// column tiles than CUs (H < 128) a column tile's token tiles are split among
-// several workgroups.
-constexpr int kXThreads = 512;                 // eight waves
+// 32 w .. +32 and all 64 tokens of a tile.  A finished token tile leaves through
+// an LDS staging area in whole rows with non-temporal stores; the k workgroups
+// also copy the tile's RoPE keys, brought into LDS with direct-to-LDS loads along
+// with the stages.  Two workgroups share each CU (74 KiB of LDS each, two waves
+// per SIMD): a barrier holds only the four waves of one workgroup, and the other
+// workgroup's waves keep the SIMD busy meanwhile.  A column tile's token tiles are
+// split among 2 CUs / (2H) workgroups.
+constexpr int kXThreads = 256;                 // four waves; two workgroups per CU
 constexpr int kXWaves = kXThreads / 64;
-constexpr int kXTok = 128;                     // tokens per token tile
+constexpr int kXTok = 64;                      // tokens per token tile
 constexpr int kXK = 128;                       // latent columns per stage
 constexpr int kXStagesPerTile = kLat / kXK;    // 4
 constexpr int kXBufs = 3;                      // ring depth
-constexpr int kXStageBytes = kXTok * kXK * 2;  // 32 KiB
+constexpr int kXStageBytes = kXTok * kXK * 2;  // 16 KiB
 constexpr int kXLoads = kXStageBytes / 1024 / kXWaves;   // 4 one-KiB loads per wave per stage
-constexpr int kXRopeBytes = kXTok * kRope * 2;           // 16 KiB of RoPE keys per token tile
+constexpr int kXRopeBytes = kXTok * kRope * 2;           // 8 KiB of RoPE keys per token tile
 constexpr int kXRopeLoads = kXRopeBytes / 1024 / kXWaves;   // 2 per wave
-constexpr int kXRowPad = 272;                  // staged output rows: 256 bytes + 16
+constexpr int kXRowPad = 272;                  // staged k rows (tokens): 256 bytes + 16
+constexpr int kXVPad = kXTok * 2 + 16;         // staged v rows (dims): 128 bytes + 16
+constexpr int kXStgBytes = kXTok * kXRowPad > 128 * kXVPad ? kXTok * kXRowPad : 128 * kXVPad;
 constexpr int kXStgOff = kXBufs * kXStageBytes;
-constexpr int kXRopeOff = kXStgOff + 128 * kXRowPad;
-constexpr int kXLdsBytes = kXRopeOff + kXRopeBytes;      // 146 KiB
+constexpr int kXRopeOff = kXStgOff + kXStgBytes;
+constexpr int kXLdsBytes = kXRopeOff + kXRopeBytes;      // 74 KiB
 static_assert(kXLoads * 1024 * kXWaves == kXStageBytes && kXRopeLoads * 1024 * kXWaves == kXRopeBytes, "");
-static_assert(kXLdsBytes <= 160 * 1024, "LDS");
+static_assert(2 * kXLdsBytes <= 160 * 1024, "LDS of two workgroups per CU");
 
 // Stage row r (one token, 256 bytes = 16 granules): granule j is stored at
 // j ^ (r & 15), so the 16 rows of a fragment read (lane (g, q): granule 4 ks + g of
-// row 16 i + q) fall in 16 different granule columns.
-__device__ __forceinline__ int xs_off(int r, int j) { return r * (kXK * 2) + ((j ^ (r & 15)) << 4); }
+// row 16 i + q) fall in 16 different granule columns.  The fragment reads use the
+// equivalent form (4 ks + g) ^ r = 4 (ks ^ (r >> 2)) + ((g ^ r) & 3).
 
 // One 16-byte direct-to-LDS load per lane from a per-lane 64-bit address: lane i
 // writes LDS[m0 + 16 i].  The wait states cover M0 written from a VALU-produced
@@ -119,14 +122,19 @@ __device__ __forceinline__ void dma16_v(const void* gaddr, uint32_t lds_addr) {
 // s_waitcnt immediate for "vector memory counter <= n", other counters untouched.
 #define XVMCNT(n) ((((n) & 15) | (((n) >> 4) << 14)) | (7 << 4) | (15 << 8))
 
-// Vector-memory operations this wave has issued after stage s's loads when it
-// waits for them at the top of iteration s (sl = s % 4; the loads of stage s + 1
-// went out at iteration s - 1; the RoPE keys of tile i go out right after stage
-// 4 i + 2; a tile's output stores go out at the end of its last stage).
+// Vector-memory operations this wave has issued after the loads of stage s + 1
+// when it waits for them in the middle of iteration s (sl = s % 4, tile ti;
+// valid while stage s + 2 exists).  Per wave, in issue order: the prologue's
+// loads of stages 0-2 and, for k, the first tile's RoPE keys; in the middle of
+// iteration s the loads of stage s + 3 and, for k at sl = 0 of a later tile, that
+// tile's RoPE keys; at the end of a tile's last stage its output stores (four,
+// six for k).
 template <bool kIsK>
-constexpr int x_younger(int sl, bool after_tile) {
-  return kXLoads + (kIsK && sl == 2 ? kXRopeLoads : 0) + (kIsK && sl == 1 ? kXRopeLoads : 0) +
-         (after_tile && (sl == 0 || sl == 1) ? (kIsK ? 6 : 4) : 0);
+constexpr int x_younger(int sl, int ti) {
+  const int rope = kIsK ? kXRopeLoads : 0;
+  const int stores = kIsK ? 6 : 4;
+  return kXLoads + ((ti == 0 && sl <= 1) || (ti > 0 && (sl == 1 || sl == 2)) ? rope : 0) +
+         (ti > 0 && sl <= 1 ? stores : 0);
 }
 // s_waitcnt takes an immediate: the counts above, spelled out (the argument is a
 // constant after unrolling, so the switch folds away).
@@ -151,8 +159,8 @@ __device__ __forceinline__ void expand_tiles(const uint16_t* __restrict__ cache,
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, r = lane & 15;
-  const int mo = 32 * (wave & 3);   // this wave's weight rows (outputs)
-  const int tb = 64 * (wave >> 2);  // this wave's tokens within a tile
+  const int mo = 32 * wave;   // this wave's weight rows (outputs)
+  const int tb = 0;           // every wave takes all 64 tokens of a tile
 
   // Weights: wf[m][k] = rows mo + 16 m + r of the head's 128, columns 32 k + 8 g .. +8.
   bf16x8_t wf[2][kLat / 32];
@@ -231,35 +239,50 @@ __device__ __forceinline__ void expand_tiles(const uint16_t* __restrict__ cache,
     for (int j = 0; j < 4; j++) acc[m][j] = f32x4_t{};
 
   const int ntiles = tt_end - tt_begin;
-  const int nst = ntiles * kXStagesPerTile;
+  const int nst = ntiles * kXStagesPerTile;   // >= 4
   if (ntiles <= 0) return;
+  // K-step ks of stage s, this wave's four token tiles: rows tb + 16 j + r, granule
+  // 4 ks + g, stored at (4 ks + g) ^ r = 4 (ks ^ (r >> 2)) + ((g ^ r) & 3): a per-lane
+  // offset per K-step, the tile j an immediate 4 KiB step.
+  const int lrow = (tb + r) * (kXK * 2) + (((g ^ r) & 3) << 4);
+  auto read_ks = [&](int s, int ks, bf16x8_t (&f)[4]) {
+    const char LDS_AS* base = lds + (s % kXBufs) * kXStageBytes + lrow + ((ks ^ (r >> 2)) << 6);
+#pragma unroll
+    for (int j = 0; j < 4; j++) f[j] = lds_b128(base + j * 16 * (kXK * 2));
+  };
   set_rows(tt_begin);
   issue(0, 0);
   issue(1, 1);
+  issue(2, 2);
+  if (kIsK) issue_rope();
+  x_wait(2 * kXLoads + (kIsK ? kXRopeLoads : 0));   // stage 0 has landed
+  __syncthreads();
+  bf16x8_t lf[4], ln[4];
+  read_ks(0, 0, lf);
   for (int ti = 0; ti < ntiles; ti++) {
     const int tile_t = (tt_begin + ti) * kXTok;
 #pragma unroll
     for (int sl = 0; sl < kXStagesPerTile; sl++) {
       const int s = ti * kXStagesPerTile + sl;
-      // Wait for this wave's loads of stage s; later ones may stay in flight.
-      if (s + 1 >= nst) __builtin_amdgcn_s_waitcnt(XVMCNT(0));
-      else if (ti > 0) x_wait(x_younger<kIsK>(sl, true));
-      else x_wait(x_younger<kIsK>(sl, false));
-      __syncthreads();   // stage s is in LDS for every wave; buffer (s + 2) % 3 is free
-      if (s + 2 < nst) {
-        if (sl == 2) set_rows(tt_begin + ti + 1);   // stage s + 2 opens the next tile
-        issue((s + 2) % kXBufs, (sl + 2) % kXStagesPerTile);
-        if (kIsK && sl == 0) issue_rope();          // this tile's RoPE keys, after stage 4 ti + 2
-      }
-      const char LDS_AS* base = lds + (s % kXBufs) * kXStageBytes;
-      bf16x8_t lf[4], ln[4];
-#pragma unroll
-      for (int j = 0; j < 4; j++) lf[j] = lds_b128(base + xs_off(tb + 16 * j + r, g));
 #pragma unroll
       for (int ks = 0; ks < kXK / 32; ks++) {
         if (ks + 1 < kXK / 32) {
-#pragma unroll
-          for (int j = 0; j < 4; j++) ln[j] = lds_b128(base + xs_off(tb + 16 * j + r, 4 * (ks + 1) + g));
+          read_ks(s, ks + 1, ln);
+        } else if (s + 1 < nst) {
+          // Before the last K-step's MFMAs (the previous K-step's are still
+          // running): stage s + 1 is in LDS for every wave and every wave is done
+          // reading stage s, whose buffer takes stage s + 3.  Then the first
+          // fragments of stage s + 1 are read under this K-step's MFMAs (after a
+          // tile's last stage: after its epilogue, which needs the registers).
+          if (s + 2 < nst) x_wait(x_younger<kIsK>(sl, ti > 0 ? 1 : 0));
+          else __builtin_amdgcn_s_waitcnt(XVMCNT(0));
+          __syncthreads();
+          if (s + 3 < nst) {
+            if (sl == 1) set_rows(tt_begin + ti + 1);   // stage s + 3 opens the next tile
+            issue(s % kXBufs, (sl + 3) % kXStagesPerTile);
+          }
+          if (kIsK && sl == 0 && ti > 0) issue_rope();   // this tile's RoPE keys
+          if (sl + 1 < kXStagesPerTile) read_ks(s + 1, 0, ln);
         }
         const int kg = sl * (kXK / 32) + ks;
 #pragma unroll
@@ -296,22 +319,24 @@ __device__ __forceinline__ void expand_tiles(const uint16_t* __restrict__ cache,
           const int tl = tb + 16 * j + 4 * g;
 #pragma unroll
           for (int e = 0; e < 4; e++) v4[e] = tile_t + tl + e < ntok ? (__bf16)acc[m][j][e] : (__bf16)0.f;
-          *reinterpret_cast<bf16x4_t LDS_AS*>(stg + (mo + 16 * m + r) * kXRowPad + tl * 2) = v4;
+          *reinterpret_cast<bf16x4_t LDS_AS*>(stg + (mo + 16 * m + r) * kXVPad + tl * 2) = v4;
         }
         acc[m][j] = f32x4_t{};
       }
     __syncthreads();   // staged tile complete; the RoPE keys landed before this stage's barrier
-    // 128 rows x 16 granules: four per thread, sixteen consecutive lanes per row.
+    // k: 64 rows x 16 granules, v: 128 rows x 8 granules; four per thread either way.
     // Non-temporal: the expanded chunk is far larger than the caches.
 #pragma unroll
     for (int u = 0; u < 4; u++) {
       const int x = tid + u * kXThreads;
-      const int gr = x & 15, row = x >> 4;
-      const i32x4_t v = *reinterpret_cast<const i32x4_t LDS_AS*>(stg + row * kXRowPad + gr * 16);
       if (kIsK) {
+        const int gr = x & 15, row = x >> 4;
+        const i32x4_t v = *reinterpret_cast<const i32x4_t LDS_AS*>(stg + row * kXRowPad + gr * 16);
         const int t = tile_t + row;
         if (t < ld) __builtin_nontemporal_store(v, reinterpret_cast<i32x4_t*>(out + ((size_t)h * ld + t) * kQK + 8 * gr));
       } else {
+        const int gr = x & 7, row = x >> 3;
+        const i32x4_t v = *reinterpret_cast<const i32x4_t LDS_AS*>(stg + row * kXVPad + gr * 16);
         const int t = tile_t + 8 * gr;   // ld is a multiple of 64: t < ld covers the granule
         if (t < ld) __builtin_nontemporal_store(v, reinterpret_cast<i32x4_t*>(out + ((size_t)h * kDv + row) * ld + t));
       }
@@ -329,12 +354,13 @@ __device__ __forceinline__ void expand_tiles(const uint16_t* __restrict__ cache,
           __builtin_nontemporal_store(v, reinterpret_cast<i32x4_t*>(out + ((size_t)h * ld + t) * kQK + kNope + 8 * part));
       }
     }
+    if (ti + 1 < ntiles) read_ks((ti + 1) * kXStagesPerTile, 0, lf);
   }
 }
 
 // Workgroup i: column tile ct = i / nsp (ct < H: k^N of head ct; else v of head
 // ct - H), token tiles [sp ntt / nsp, (sp + 1) ntt / nsp) with sp = i % nsp.
-__global__ __launch_bounds__(kXThreads, 1) void mla_expand_kv_kernel(const uint16_t* __restrict__ cache,
+__global__ __launch_bounds__(kXThreads, 2) void mla_expand_kv_kernel(const uint16_t* __restrict__ cache,
                                                                     const int32_t* __restrict__ block_table, int t0,
                                                                     int ntok, int ld, int num_pages,
                                                                     const uint16_t* __restrict__ w_uk,
@@ -601,11 +627,11 @@ hipError_t launch_expand_kv(const uint16_t* cache, const int32_t* block_table, i
   int ld = (ntok + 63) / 64 * 64;
   int ntt = (ld + kXTok - 1) / kXTok;
   const int nct = 2 * H;
-  // One workgroup per CU: a column tile's token tiles are split among cus / nct workgroups.
+  // Two workgroups per CU: a column tile's token tiles are split among 2 cus / nct workgroups.
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
-  int nsp = cus / nct > 1 ? cus / nct : 1;
+  int nsp = 2 * cus / nct > 1 ? 2 * cus / nct : 1;
   nsp = nsp < ntt ? nsp : ntt;
   void* args[] = {(void*)&cache, (void*)&block_table, (void*)&t0,    (void*)&ntok,   (void*)&ld, (void*)&num_pages,
                   (void*)&w_uk,  (void*)&w_uv,        (void*)&k_out, (void*)&vt_out, (void*)&H,  (void*)&ntt,
