@@ -274,23 +274,34 @@ def bench_prefill(torch, M, W, name, launches=10):
     pw = W.make_prefill_workload(name, num_heads=H, num_new=n, seqlen=L, seed=1, poison=False)
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16) if a.dtype == np.uint16 else a).to("cuda")
     q, kv, bt, wuk, wuv = dev(pw.q), dev(pw.cache), dev(pw.block_table), dev(pw.w_uk), dev(pw.w_uv)
-    pre = M.MlaPrefill(num_heads=H, num_new=n, seqlen=L, num_pages=pw.num_pages, max_blocks=len(pw.block_table),
-                       chunk_tokens=cfg["chunk_tokens"])
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    keep_busy(torch, lambda i: pre(q, kv, bt, wuk, wuv), seconds=0.1, min_calls=3)
-    e0.record()
-    for _ in range(launches):
-        pre(q, kv, bt, wuk, wuv)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / launches
     flops = prefill_counts(H, n, L)
-    tflops = flops / (ms * 1e-3) / 1e12
-    return {"workload": name, "heads": H, "new_tokens": n, "seqlen": L, "chunk_tokens": cfg["chunk_tokens"],
-            "ms": round(ms, 4), "gflop": round(flops / 1e9, 1), "tflops": round(tflops, 1),
-            "frac_mfma": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
-            "timing": f"{launches} back-to-back calls between one event pair, after the timed region; "
-                      "not part of the step"}
+
+    def timed(chunk_tokens):
+        pre = M.MlaPrefill(num_heads=H, num_new=n, seqlen=L, num_pages=pw.num_pages, max_blocks=len(pw.block_table),
+                           chunk_tokens=chunk_tokens)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        keep_busy(torch, lambda i: pre(q, kv, bt, wuk, wuv), seconds=0.1, min_calls=3)
+        e0.record()
+        for _ in range(launches):
+            pre(q, kv, bt, wuk, wuv)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / launches
+        tflops = flops / (ms * 1e-3) / 1e12
+        del pre
+        return {"chunk_tokens": chunk_tokens, "ms": round(ms, 4), "tflops": round(tflops, 1),
+                "frac_mfma": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4)}
+
+    res = {"workload": name, "heads": H, "new_tokens": n, "seqlen": L, "gflop": round(flops / 1e9, 1)}
+    res.update(timed(cfg["chunk_tokens"]))
+    whole = -(-L // 64) * 64
+    if whole != cfg["chunk_tokens"]:
+        # The same call with the whole context expanded at once (its K and V take
+        # L x H x 640 bytes: 2.7 GB for the extend, which HBM holds easily).
+        res["one_chunk"] = timed(whole)
+    res["timing"] = (f"{launches} back-to-back calls between one event pair per chunk size, after the timed region; "
+                     "not part of the step")
+    return res
 
 
 def oracle_rows(wl, rows):

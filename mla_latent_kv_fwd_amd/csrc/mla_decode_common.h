@@ -128,10 +128,11 @@ __device__ __forceinline__ void store_partial(const DecodeArgs& a, size_t pbase,
   __syncthreads();
   typedef int i32x4_st __attribute__((ext_vector_type(4)));
   char* pout = a.ws + a.lay.part_out + pbase * (kHeadDimV * 2);
-  // 128 rows x 64 granules over 512 threads: thread x moves granule x & 63 of
-  // rows x / 64 + 8i, i = 0..15, read four at a time so the LDS latency is
-  // paid four times rather than sixteen.
-  static_assert(kRowsPerBlock * (kHeadDimV * 2 / 16) == 16 * kThreads, "");
+  // kRowsPerBlock rows x 64 granules over the workgroup: thread x moves granule
+  // x & 63 of rows x / 64 + (kThreads / 64) i, i = 0..15, read four at a time so
+  // the LDS latency is paid four times rather than sixteen.
+  constexpr int kRowStep = kThreads / 64;
+  static_assert(kRowsPerBlock * (kHeadDimV * 2 / 16) == 16 * kThreads, "16 granules per thread");
   const int x0 = (int)threadIdx.x;
   const char LDS_AS* src = stage + (x0 >> 6) * kPitch + (x0 & 63) * 16;
   char* dst = pout + (size_t)(x0 >> 6) * (kHeadDimV * 2) + (x0 & 63) * 16;
@@ -139,9 +140,9 @@ __device__ __forceinline__ void store_partial(const DecodeArgs& a, size_t pbase,
   for (int h = 0; h < 4; h++) {
     i32x4_st v[4];
 #pragma unroll
-    for (int j = 0; j < 4; j++) v[j] = *reinterpret_cast<const i32x4_st LDS_AS*>(src + (4 * h + j) * 8 * kPitch);
+    for (int j = 0; j < 4; j++) v[j] = *reinterpret_cast<const i32x4_st LDS_AS*>(src + (4 * h + j) * kRowStep * kPitch);
 #pragma unroll
-    for (int j = 0; j < 4; j++) *reinterpret_cast<i32x4_st*>(dst + (4 * h + j) * 8 * (kHeadDimV * 2)) = v[j];
+    for (int j = 0; j < 4; j++) *reinterpret_cast<i32x4_st*>(dst + (4 * h + j) * kRowStep * (kHeadDimV * 2)) = v[j];
   }
 }
 
