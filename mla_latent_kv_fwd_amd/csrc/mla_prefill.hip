@@ -79,10 +79,10 @@ __device__ __forceinline__ float row_sum(float x) {
 // latent is thus the only operand loaded per token tile: 64 KiB for 8.4 MFLOP
 // (128 FLOP per byte, 32 B/clk per CU at the matrix pipe's full rate, under the
 // ~54 B/clk a CU's direct-to-LDS loads sustain).  Wave w covers weight rows
-// 32 w .. +32 and all 64 tokens of a tile.  A finished token tile leaves through
-// an LDS staging area in whole rows with non-temporal stores; the k workgroups
-// also copy the tile's RoPE keys, brought into LDS with direct-to-LDS loads along
-// with the stages.  Two workgroups share each CU (74 KiB of LDS each, two waves
+// 32 w .. +32 and all 64 tokens of a tile.  A finished token tile is staged in
+// LDS and leaves in whole rows with non-temporal stores issued at the next tile's
+// first barrier; the k workgroups also copy the tile's RoPE keys, brought into LDS
+// with direct-to-LDS loads along with the stages.  Two workgroups share each CU (74 KiB of LDS each, two waves
 // per SIMD): a barrier holds only the four waves of one workgroup, and the other
 // workgroup's waves keep the SIMD busy meanwhile.  A column tile's token tiles are
 // split among 2 CUs / (2H) workgroups.
@@ -126,15 +126,14 @@ __device__ __forceinline__ void dma16_v(const void* gaddr, uint32_t lds_addr) {
 // when it waits for them in the middle of iteration s (sl = s % 4, tile ti;
 // valid while stage s + 2 exists).  Per wave, in issue order: the prologue's
 // loads of stages 0-2 and, for k, the first tile's RoPE keys; in the middle of
-// iteration s the loads of stage s + 3 and, for k at sl = 0 of a later tile, that
-// tile's RoPE keys; at the end of a tile's last stage its output stores (four,
-// six for k).
+// iteration s: at sl = 0 of a later tile the previous tile's output stores (four,
+// six for k), at sl = 1 of a later tile (k) that tile's RoPE keys, then the loads
+// of stage s + 3.
 template <bool kIsK>
 constexpr int x_younger(int sl, int ti) {
   const int rope = kIsK ? kXRopeLoads : 0;
   const int stores = kIsK ? 6 : 4;
-  return kXLoads + ((ti == 0 && sl <= 1) || (ti > 0 && (sl == 1 || sl == 2)) ? rope : 0) +
-         (ti > 0 && sl <= 1 ? stores : 0);
+  return kXLoads + (ti == 0 ? (sl <= 1 ? rope : 0) : (sl == 1 ? stores : 0) + (sl == 2 ? rope : 0));
 }
 // s_waitcnt takes an immediate: the counts above, spelled out (the argument is a
 // constant after unrolling, so the switch folds away).
@@ -250,60 +249,14 @@ __device__ __forceinline__ void expand_tiles(const uint16_t* __restrict__ cache,
 #pragma unroll
     for (int j = 0; j < 4; j++) f[j] = lds_b128(base + j * 16 * (kXK * 2));
   };
-  set_rows(tt_begin);
-  issue(0, 0);
-  issue(1, 1);
-  issue(2, 2);
-  if (kIsK) issue_rope();
-  x_wait(2 * kXLoads + (kIsK ? kXRopeLoads : 0));   // stage 0 has landed
-  __syncthreads();
-  bf16x8_t lf[4], ln[4];
-  read_ks(0, 0, lf);
-  for (int ti = 0; ti < ntiles; ti++) {
-    const int tile_t = (tt_begin + ti) * kXTok;
-#pragma unroll
-    for (int sl = 0; sl < kXStagesPerTile; sl++) {
-      const int s = ti * kXStagesPerTile + sl;
-#pragma unroll
-      for (int ks = 0; ks < kXK / 32; ks++) {
-        if (ks + 1 < kXK / 32) {
-          read_ks(s, ks + 1, ln);
-        } else if (s + 1 < nst) {
-          // Before the last K-step's MFMAs (the previous K-step's are still
-          // running): stage s + 1 is in LDS for every wave and every wave is done
-          // reading stage s, whose buffer takes stage s + 3.  Then the first
-          // fragments of stage s + 1 are read under this K-step's MFMAs (after a
-          // tile's last stage: after its epilogue, which needs the registers).
-          if (s + 2 < nst) x_wait(x_younger<kIsK>(sl, ti > 0 ? 1 : 0));
-          else __builtin_amdgcn_s_waitcnt(XVMCNT(0));
-          __syncthreads();
-          if (s + 3 < nst) {
-            if (sl == 1) set_rows(tt_begin + ti + 1);   // stage s + 3 opens the next tile
-            issue(s % kXBufs, (sl + 3) % kXStagesPerTile);
-          }
-          if (kIsK && sl == 0 && ti > 0) issue_rope();   // this tile's RoPE keys
-          if (sl + 1 < kXStagesPerTile) read_ks(s + 1, 0, ln);
-        }
-        const int kg = sl * (kXK / 32) + ks;
-#pragma unroll
-        for (int m = 0; m < 2; m++)
-#pragma unroll
-          for (int j = 0; j < 4; j++)
-            acc[m][j] = kIsK ? __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[m][kg], lf[j], acc[m][j], 0, 0, 0)
-                             : __builtin_amdgcn_mfma_f32_16x16x32_bf16(lf[j], wf[m][kg], acc[m][j], 0, 0, 0);
-#pragma unroll
-        for (int j = 0; j < 4; j++) lf[j] = ln[j];
-        __builtin_amdgcn_sched_barrier(0);   // keep the next K-step's reads ahead of these MFMAs
-      }
-    }
-
-    // Epilogue of the tile.  Lane (g, r) holds, for k, C[n = mo + 16 m + 4 g + e][t = tb + 16 j + r]
-    // and, for v, C[t = tb + 16 j + 4 g + e][v = mo + 16 m + r].  The staged tile is
-    // [row][128 values] in bf16 with 272-byte rows: k rows are tokens (values: the
-    // head's 128 outputs), v rows are dims (values: the tile's 128 tokens).  Tokens
-    // past the range are written as zeros.  (The staging area was last read four
-    // barriers ago.)
-    char LDS_AS* stg = lds + kXStgOff;
+  char LDS_AS* stg = lds + kXStgOff;
+  // A finished tile: the accumulators into the LDS staging area (then cleared).
+  auto stage_tile = [&](int tile_t) {
+    // Lane (g, r) holds, for k, C[n = mo + 16 m + 4 g + e][t = tb + 16 j + r] and,
+    // for v, C[t = tb + 16 j + 4 g + e][v = mo + 16 m + r].  The staged tile is bf16
+    // rows: k rows are tokens (272 bytes: the head's 128 outputs + 16), v rows are
+    // dims (144 bytes: the tile's 64 tokens + 16).  Tokens past the range are written
+    // as zeros.  (The staging area was last read three barriers ago.)
 #pragma unroll
     for (int m = 0; m < 2; m++)
 #pragma unroll
@@ -323,7 +276,11 @@ __device__ __forceinline__ void expand_tiles(const uint16_t* __restrict__ cache,
         }
         acc[m][j] = f32x4_t{};
       }
-    __syncthreads();   // staged tile complete; the RoPE keys landed before this stage's barrier
+  };
+  // A staged tile leaves in whole rows: at the first barrier of the next tile,
+  // under that stage's last MFMAs (every wave's staging writes precede the
+  // barrier), or after the last tile.
+  auto store_tile = [&](int tile_t) {
     // k: 64 rows x 16 granules, v: 128 rows x 8 granules; four per thread either way.
     // Non-temporal: the expanded chunk is far larger than the caches.
 #pragma unroll
@@ -354,8 +311,63 @@ __device__ __forceinline__ void expand_tiles(const uint16_t* __restrict__ cache,
           __builtin_nontemporal_store(v, reinterpret_cast<i32x4_t*>(out + ((size_t)h * ld + t) * kQK + kNope + 8 * part));
       }
     }
+  };
+  set_rows(tt_begin);
+  issue(0, 0);
+  issue(1, 1);
+  issue(2, 2);
+  if (kIsK) issue_rope();
+  x_wait(2 * kXLoads + (kIsK ? kXRopeLoads : 0));   // stage 0 has landed
+  __syncthreads();
+  bf16x8_t lf[4], ln[4];
+  read_ks(0, 0, lf);
+  for (int ti = 0; ti < ntiles; ti++) {
+    const int tile_t = (tt_begin + ti) * kXTok;
+#pragma unroll
+    for (int sl = 0; sl < kXStagesPerTile; sl++) {
+      const int s = ti * kXStagesPerTile + sl;
+#pragma unroll
+      for (int ks = 0; ks < kXK / 32; ks++) {
+        if (ks + 1 < kXK / 32) {
+          read_ks(s, ks + 1, ln);
+        } else if (s + 1 < nst) {
+          // Before the last K-step's MFMAs (the previous K-step's are still
+          // running): stage s + 1 is in LDS for every wave and every wave is done
+          // reading stage s, whose buffer takes stage s + 3.  Then the first
+          // fragments of stage s + 1 are read under this K-step's MFMAs (after a
+          // tile's last stage: after its epilogue, which needs the registers).
+          if (s + 2 < nst) x_wait(x_younger<kIsK>(sl, ti > 0 ? 1 : 0));
+          else __builtin_amdgcn_s_waitcnt(XVMCNT(0));
+          __syncthreads();
+          // The previous tile, staged before this barrier, leaves now; the next
+          // barrier retires its reads of the staging and RoPE areas before this
+          // tile's RoPE keys overwrite the latter.
+          if (sl == 0 && ti > 0) store_tile(tile_t - kXTok);
+          if (kIsK && sl == 1 && ti > 0) issue_rope();   // this tile's RoPE keys
+          if (s + 3 < nst) {
+            if (sl == 1) set_rows(tt_begin + ti + 1);   // stage s + 3 opens the next tile
+            issue(s % kXBufs, (sl + 3) % kXStagesPerTile);
+          }
+          if (sl + 1 < kXStagesPerTile) read_ks(s + 1, 0, ln);
+        }
+        const int kg = sl * (kXK / 32) + ks;
+#pragma unroll
+        for (int m = 0; m < 2; m++)
+#pragma unroll
+          for (int j = 0; j < 4; j++)
+            acc[m][j] = kIsK ? __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[m][kg], lf[j], acc[m][j], 0, 0, 0)
+                             : __builtin_amdgcn_mfma_f32_16x16x32_bf16(lf[j], wf[m][kg], acc[m][j], 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < 4; j++) lf[j] = ln[j];
+        __builtin_amdgcn_sched_barrier(0);   // keep the next K-step's reads ahead of these MFMAs
+      }
+    }
+
+    stage_tile(tile_t);
     if (ti + 1 < ntiles) read_ks((ti + 1) * kXStagesPerTile, 0, lf);
   }
+  __syncthreads();   // the last tile is staged
+  store_tile((tt_end - 1) * kXTok);
 }
 
 // Workgroup i: column tile ct = i / nsp (ct < H: k^N of head ct; else v of head
