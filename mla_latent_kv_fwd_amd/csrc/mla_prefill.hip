@@ -82,10 +82,10 @@ __device__ __forceinline__ float row_sum(float x) {
 // 32 w .. +32 and all 64 tokens of a tile.  A finished token tile is staged in
 // LDS and leaves in whole rows with non-temporal stores issued at the next tile's
 // first barrier; the k workgroups also copy the tile's RoPE keys, brought into LDS
-// with direct-to-LDS loads along with the stages.  Two workgroups share each CU (74 KiB of LDS each, two waves
-// per SIMD): a barrier holds only the four waves of one workgroup, and the other
-// workgroup's waves keep the SIMD busy meanwhile.  A column tile's token tiles are
-// split among 2 CUs / (2H) workgroups.
+// with direct-to-LDS loads along with the stages.  Two workgroups share each CU
+// (74 KiB of LDS each, two waves per SIMD): a barrier holds only the four waves of
+// one workgroup, and the other workgroup's waves keep the SIMD busy meanwhile.  A
+// column tile's token tiles are split among 2 CUs / (2H) workgroups.
 constexpr int kXThreads = 256;                 // four waves; two workgroups per CU
 constexpr int kXWaves = kXThreads / 64;
 constexpr int kXTok = 64;                      // tokens per token tile
@@ -135,8 +135,8 @@ constexpr int x_younger(int sl, int ti) {
   const int stores = kIsK ? 6 : 4;
   return kXLoads + (ti == 0 ? (sl <= 1 ? rope : 0) : (sl == 1 ? stores : 0) + (sl == 2 ? rope : 0));
 }
-// s_waitcnt takes an immediate: the counts above, spelled out (the argument is a
-// constant after unrolling, so the switch folds away).
+// s_waitcnt takes an immediate: the counts above, spelled out (sl is a constant
+// after unrolling; whether the tile is the first is a uniform scalar branch).
 __device__ __forceinline__ void x_wait(int n) {
   switch (n) {
     case 4: __builtin_amdgcn_s_waitcnt(XVMCNT(4)); break;
