@@ -522,15 +522,31 @@ __global__ __launch_bounds__(kAttThreads, 1) void mla_prefill_attention_kernel(
       f32x4_t s[2][2];   // [query tile][score tile a/b]
 #pragma unroll
       for (int qt = 0; qt < 2; qt++) s[qt][0] = s[qt][1] = f32x4_t{};
+      // K fragments read three K-steps ahead, pinned there (the compiler would
+      // read them one or two K-steps ahead and wait on each pair).
+      auto read_ka = [&](int ks) { return lds_b128(base + k_off(32 * grp + ta, 4 * ks + g)); };
+      auto read_kb = [&](int ks) { return lds_b128(base + k_off(32 * grp + ta + 4, 4 * ks + g)); };
+      bf16x8_t a0 = read_ka(0), b0 = read_kb(0), a1 = read_ka(1), b1 = read_kb(1);
+      bf16x8_t a2 = read_ka(2), b2 = read_kb(2);
 #pragma unroll
       for (int ks = 0; ks < kQK / 32; ks++) {
-        const bf16x8_t ka = lds_b128(base + k_off(32 * grp + ta, 4 * ks + g));
-        const bf16x8_t kbf = lds_b128(base + k_off(32 * grp + ta + 4, 4 * ks + g));
+        bf16x8_t a3 = a2, b3 = b2;
+        if (ks + 3 < kQK / 32) {
+          a3 = read_ka(ks + 3);
+          b3 = read_kb(ks + 3);
+        }
 #pragma unroll
         for (int qt = 0; qt < 2; qt++) {
-          s[qt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[qt][ks], s[qt][0], 0, 0, 0);
-          s[qt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kbf, qf[qt][ks], s[qt][1], 0, 0, 0);
+          s[qt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[qt][ks], s[qt][0], 0, 0, 0);
+          s[qt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b0, qf[qt][ks], s[qt][1], 0, 0, 0);
         }
+        a0 = a1;
+        b0 = b1;
+        a1 = a2;
+        b1 = b2;
+        a2 = a3;
+        b2 = b3;
+        __builtin_amdgcn_sched_barrier(0);
       }
       // s[qt][0][e] is token 32 grp + 8g + e, s[qt][1][e] token 32 grp + 8g + 4 + e.
       bf16x8_t pb[2];
@@ -571,11 +587,21 @@ __global__ __launch_bounds__(kAttThreads, 1) void mla_prefill_attention_kernel(
         }
       }
       // O^T[d][query] += V^T[d][token] . P^T[token][query]: A = 16 dims x 32 tokens of V^T.
+      // V^T fragments read three dim tiles ahead, pinned there: otherwise the
+      // compiler reads each right before its MFMAs and every pair waits a full LDS
+      // latency.
+      auto read_vf = [&](int dt) { return lds_b128(base + v_off(16 * dt + r, 4 * grp + g)); };
+      bf16x8_t v0 = read_vf(0), v1 = read_vf(1), v2 = read_vf(2);
 #pragma unroll
       for (int dt = 0; dt < kDv / 16; dt++) {
-        const bf16x8_t vf = lds_b128(base + v_off(16 * dt + r, 4 * grp + g));
+        bf16x8_t v3 = v2;
+        if (dt + 3 < kDv / 16) v3 = read_vf(dt + 3);
 #pragma unroll
-        for (int qt = 0; qt < 2; qt++) o[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[qt], o[qt][dt], 0, 0, 0);
+        for (int qt = 0; qt < 2; qt++) o[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v0, pb[qt], o[qt][dt], 0, 0, 0);
+        v0 = v1;
+        v1 = v2;
+        v2 = v3;
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
