@@ -94,7 +94,10 @@ int mla_prefill_workspace_size(const mla_prefill_params* p, size_t* bytes);
 /*
  * The whole expand path, chunk by chunk: for each chunk of chunk_tokens positions,
  * mla_expand_kv then mla_prefill_attention into the chunk's partial, then one
- * mla_lse_merge.  q: bf16 [n][H][192]; out: bf16 [n][H][128]; lse: fp32 [n][H].
+ * mla_lse_merge.  When one chunk covers the whole context (chunk_tokens >= seqlen)
+ * the attention writes out and lse itself and no merge runs (the same numbers: a
+ * merge of a single part only rounds it to bf16).  q: bf16 [n][H][192]; out: bf16
+ * [n][H][128]; lse: fp32 [n][H].
  * workspace: device memory of at least mla_prefill_workspace_size bytes, 256-byte aligned.
  */
 int mla_chunked_prefill(const mla_prefill_params* p, const void* q, const void* kv_cache, const int32_t* block_table,

@@ -319,7 +319,7 @@ int mla_prefill_attention(const mla_prefill_params* p, const void* q, const void
   if (t0 < 0 || ntok < 1 || ntok > kMaxChunkTokens || (int64_t)t0 + ntok > p->seqlen) return MLA_ERR_INVALID_ARG;
   if (launch_prefill_attention(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                static_cast<const uint16_t*>(vt), t0, ntok, p->num_new, p->seqlen, p->num_heads,
-                               p->softmax_scale, out, lse, (hipStream_t)stream) != hipSuccess)
+                               p->softmax_scale, out, lse, nullptr, (hipStream_t)stream) != hipSuccess)
     return MLA_ERR_HIP;
   return MLA_OK;
 }
@@ -362,6 +362,9 @@ int mla_chunked_prefill(const mla_prefill_params* p, const void* q, const void* 
   float* lparts = reinterpret_cast<float*>(ws + l.lparts);
   const size_t rows = (size_t)p->num_new * p->num_heads;
   const hipStream_t s = (hipStream_t)stream;
+  // One chunk: the attention writes the final bf16 rows and LSEs itself (the merge
+  // of a single part is the identity up to that rounding).
+  const bool single = l.nchunks == 1;
   for (int j = 0; j < l.nchunks; j++) {
     const int t0 = j * p->chunk_tokens;
     const int ntok = p->seqlen - t0 < p->chunk_tokens ? p->seqlen - t0 : p->chunk_tokens;
@@ -370,11 +373,13 @@ int mla_chunked_prefill(const mla_prefill_params* p, const void* q, const void* 
                          p->num_heads, s) != hipSuccess)
       return MLA_ERR_HIP;
     if (launch_prefill_attention(static_cast<const uint16_t*>(q), kbuf, vtbuf, t0, ntok, p->num_new, p->seqlen,
-                                 p->num_heads, p->softmax_scale, parts + (size_t)j * rows * 128,
-                                 lparts + (size_t)j * rows, s) != hipSuccess)
+                                 p->num_heads, p->softmax_scale, single ? nullptr : parts + (size_t)j * rows * 128,
+                                 single ? lse : lparts + (size_t)j * rows,
+                                 single ? static_cast<uint16_t*>(out) : nullptr, s) != hipSuccess)
       return MLA_ERR_HIP;
   }
-  if (launch_lse_merge((int)rows, l.nchunks, parts, lparts, static_cast<uint16_t*>(out), lse, s) != hipSuccess)
+  if (!single &&
+      launch_lse_merge((int)rows, l.nchunks, parts, lparts, static_cast<uint16_t*>(out), lse, s) != hipSuccess)
     return MLA_ERR_HIP;
   return MLA_OK;
 }

@@ -37,8 +37,11 @@ hipError_t launch_project_out(const uint16_t* o_latent, const uint16_t* w_uv, ui
 hipError_t launch_expand_kv(const uint16_t* cache, const int32_t* block_table, int t0, int ntok, int num_pages,
                             const uint16_t* w_uk, const uint16_t* w_uv, uint16_t* k_out, uint16_t* vt_out, int H,
                             hipStream_t stream);
+// out16 non-null: the rows go out in bf16 to out16 (final output of a single-chunk
+// call) instead of fp32 to out.
 hipError_t launch_prefill_attention(const uint16_t* q, const uint16_t* k, const uint16_t* vt, int t0, int ntok, int n,
-                                    int L, int H, float softmax_scale, float* out, float* lse, hipStream_t stream);
+                                    int L, int H, float softmax_scale, float* out, float* lse, uint16_t* out16,
+                                    hipStream_t stream);
 hipError_t launch_lse_merge(int rows, int J, const float* parts, const float* lparts, uint16_t* out, float* lse,
                             hipStream_t stream);
 

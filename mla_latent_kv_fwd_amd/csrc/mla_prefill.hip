@@ -414,7 +414,8 @@ __device__ __forceinline__ int v_off(int d, int j) { return kKBytes + d * (kKBlk
 
 __global__ __launch_bounds__(kAttThreads, 1) void mla_prefill_attention_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kbuf, const uint16_t* __restrict__ vtbuf, int t0,
-    int ntok, int ld, int n, int L, int H, float scale_log2, float* __restrict__ out, float* __restrict__ lse) {
+    int ntok, int ld, int n, int L, int H, float scale_log2, float* __restrict__ out, float* __restrict__ lse,
+    uint16_t* __restrict__ out16) {
   __shared__ __attribute__((aligned(1024))) char smem[kAttBufs * kStage];
   char LDS_AS* lds = (char LDS_AS*)smem;
   const uint32_t lds_addr = (uint32_t)(uintptr_t)smem;
@@ -606,16 +607,31 @@ __global__ __launch_bounds__(kAttThreads, 1) void mla_prefill_attention_kernel(
     }
   }
 
-  // Finalise: lane (g, r) holds O^T[16 dt + 4g + e][query qw + 16 qt + r].
+  // Finalise: lane (g, r) holds O^T[16 dt + 4g + e][query qw + 16 qt + r].  The
+  // normalised rows go out in fp32 (a chunk's part, merged later), or, when the
+  // chunk is the whole context, in bf16 as the final output (the merge of a single
+  // part would round the same fp32 numbers the same way).
 #pragma unroll
   for (int qt = 0; qt < 2; qt++) {
     const float ltot = row_sum(lsum[qt]);
     const int qi = qw + 16 * qt + r;
     if (qi >= n) continue;
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-    float* orow = out + ((size_t)qi * H + h) * kDv + 4 * g;
+    if (out16) {   // uniform
+      uint16_t* orow = out16 + ((size_t)qi * H + h) * kDv + 4 * g;
 #pragma unroll
-    for (int dt = 0; dt < kDv / 16; dt++) *reinterpret_cast<f32x4_t*>(orow + 16 * dt) = o[qt][dt] * inv;
+      for (int dt = 0; dt < kDv / 16; dt++) {
+        const f32x4_t x = o[qt][dt] * inv;
+        bf16x4_t w;
+#pragma unroll
+        for (int e = 0; e < 4; e++) w[e] = (__bf16)x[e];
+        *reinterpret_cast<bf16x4_t*>(orow + 16 * dt) = w;
+      }
+    } else {
+      float* orow = out + ((size_t)qi * H + h) * kDv + 4 * g;
+#pragma unroll
+      for (int dt = 0; dt < kDv / 16; dt++) *reinterpret_cast<f32x4_t*>(orow + 16 * dt) = o[qt][dt] * inv;
+    }
     if (g == 0) lse[(size_t)qi * H + h] = ltot > 0.f ? (m_ref[qt] + __builtin_amdgcn_logf(ltot)) * kLn2 : -INFINITY;
   }
 }
@@ -678,11 +694,12 @@ hipError_t launch_expand_kv(const uint16_t* cache, const int32_t* block_table, i
 }
 
 hipError_t launch_prefill_attention(const uint16_t* q, const uint16_t* k, const uint16_t* vt, int t0, int ntok, int n,
-                                    int L, int H, float softmax_scale, float* out, float* lse, hipStream_t stream) {
+                                    int L, int H, float softmax_scale, float* out, float* lse, uint16_t* out16,
+                                    hipStream_t stream) {
   int ld = (ntok + 63) / 64 * 64;
   float scale_log2 = softmax_scale * 1.4426950408889634f;
   void* args[] = {(void*)&q, (void*)&k, (void*)&vt, (void*)&t0, (void*)&ntok, (void*)&ld, (void*)&n,
-                  (void*)&L, (void*)&H, (void*)&scale_log2, (void*)&out, (void*)&lse};
+                  (void*)&L, (void*)&H, (void*)&scale_log2, (void*)&out, (void*)&lse, (void*)&out16};
   return hipLaunchKernel((const void*)mla_prefill_attention_kernel, dim3((n + kAttQ - 1) / kAttQ, H),
                          dim3(kAttThreads), args, 0, stream);
 }

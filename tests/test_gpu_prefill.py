@@ -241,14 +241,42 @@ def test_prefill_block_table_permutation_is_bit_exact(torch, M):
     assert np.array_equal(o1, o2) and np.array_equal(l1.view(np.uint32), l2.view(np.uint32))
 
 
-def test_extend_after_32k_prefix_sampled(torch, M):
-    """The handbook's "+512 new tokens after a 32K prefix" at 128 heads, chunks of 8,192: the GPU computes
-    everything; the oracle computes 3 query rows of 2 heads."""
+@pytest.mark.parametrize("chunk", [8192, 33280])
+def test_extend_after_32k_prefix_sampled(torch, M, chunk):
+    """The handbook's "+512 new tokens after a 32K prefix" at 128 heads, in chunks of 8,192 and as one chunk of
+    the whole context: the GPU computes everything; the oracle computes 3 query rows of 2 heads."""
     pw = W.make_prefill_workload("extend", num_heads=128, num_new=512, seqlen=32768 + 512, seed=8)
-    _say("extend 32K + 512, H=128 (sampled)")
-    out, lse = _run_chunked(torch, M, pw, 8192)
+    _say(f"extend 32K + 512, H=128, chunk {chunk} (sampled)")
+    out, lse = _run_chunked(torch, M, pw, chunk)
     rows, heads = np.array([0, 256, 511]), np.array([5, 127])
     ref_o, ref_l, lb = _oracle_expand(pw, rows=rows, heads=heads)
     got_o = _f64(out)[rows][:, heads]
     got_l = lse[rows][:, heads]
     _check_rows(got_o, got_l, ref_o, ref_l, "extend sampled", lse_bound=lb)
+
+
+@pytest.mark.parametrize("H,n,L", [(16, 300, 300), (8, 150, 2000), (128, 40, 700)])
+def test_single_chunk_equals_expand_attend_merge(torch, M, H, n, L):
+    """A call whose one chunk covers the context skips the merge: its bf16 rows and LSEs must be bit-identical to
+    expansion, attention into an fp32 part and a merge of that single part, run as separate calls."""
+    pw = W.make_prefill_workload("one", num_heads=H, num_new=n, seqlen=L, seed=H + n + L)
+    _say(f"single chunk vs expand/attend/merge H={H} n={n} L={L}")
+    o1, l1 = _run_chunked(torch, M, pw, -(-L // 64) * 64)
+    p = _params(M, pw, -(-L // 64) * 64)
+    ld = -(-L // 64) * 64
+    s = torch.cuda.current_stream().cuda_stream
+    cache, bt = _dev(torch, pw.cache), _dev(torch, pw.block_table)
+    wuk, wuv, q = _dev(torch, pw.w_uk), _dev(torch, pw.w_uv), _dev(torch, pw.q)
+    k = torch.empty((H, ld, 192), dtype=torch.int16, device="cuda")
+    vt = torch.empty((H, 128, ld), dtype=torch.int16, device="cuda")
+    part = torch.empty((n, H, 128), dtype=torch.float32, device="cuda")
+    lpart = torch.empty((n, H), dtype=torch.float32, device="cuda")
+    out = torch.empty((n, H, 128), dtype=torch.int16, device="cuda")
+    lse = torch.empty((n, H), dtype=torch.float32, device="cuda")
+    M.mla_expand_kv(p, cache.data_ptr(), bt.data_ptr(), 0, L, wuk.data_ptr(), wuv.data_ptr(), k.data_ptr(),
+                    vt.data_ptr(), s)
+    M.mla_prefill_attention(p, q.data_ptr(), k.data_ptr(), vt.data_ptr(), 0, L, part.data_ptr(), lpart.data_ptr(), s)
+    M.mla_lse_merge(n * H, 1, part.data_ptr(), lpart.data_ptr(), out.data_ptr(), lse.data_ptr(), s)
+    o2, l2 = _bits(torch, out), lse.cpu().numpy()
+    assert np.array_equal(o1.reshape(-1), o2.reshape(-1))
+    assert np.array_equal(l1.reshape(-1).view(np.uint32), l2.reshape(-1).view(np.uint32))
