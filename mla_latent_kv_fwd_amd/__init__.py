@@ -54,6 +54,31 @@ class MlaError(RuntimeError):
         self.status = status
 
 
+class MlaDeviceError(RuntimeError):
+    """Debug mode only: the device-side values of a decode call were invalid (found before the launch by the
+    synchronous checks, or reported by the kernels in the workspace flags after it)."""
+
+    def __init__(self, message: str, flags: int = 0):
+        super().__init__(message)
+        self.flags = flags
+
+
+_FLAG_TEXT = ((0x1, "a sequence length outside [seqlen_q, max_blocks_per_seq * 64] was clamped"),
+              (0x2, "a referenced block-table entry was outside [0, num_pages)"),
+              (0x4, "the workspace held no plan for these parameters"))
+
+
+def describe_flags(flags: int) -> str:
+    """The workspace flag bits as text."""
+    parts = [t for bit, t in _FLAG_TEXT if flags & bit]
+    return "; ".join(parts) if parts else "none"
+
+
+def debug_from_env() -> bool:
+    """MLA_DEBUG=1 in the environment turns on MlaDecode's debug mode by default."""
+    return os.environ.get("MLA_DEBUG", "") not in ("", "0")
+
+
 class DecodeParams(ctypes.Structure):
     """Mirror of mla_decode_params."""
     _fields_ = [("batch", ctypes.c_int32), ("seqlen_q", ctypes.c_int32), ("num_heads", ctypes.c_int32),
@@ -360,9 +385,14 @@ class MlaDecode:
 
     def __init__(self, *, batch, seqlen_q, num_heads, num_pages, max_blocks_per_seq, kv_dtype=MLA_KV_BF16,
                  causal=False, softmax_scale=SOFTMAX_SCALE, num_workgroups=0, fp8_path=MLA_FP8_PATH_EXACT,
-                 device="cuda"):
+                 device="cuda", debug=None):
         import torch
         self.torch = torch
+        # Debug mode: before each decode, synchronous checks of the device-side values the kernels otherwise
+        # only clamp and flag (every length in [seqlen_q, max_blocks_per_seq * 64], every block-table entry a
+        # request uses in [0, num_pages)); after decode + combine, any workspace flag raises MlaDeviceError.
+        # Each check synchronises the stream: for testing and bring-up, not for timing.
+        self.debug = debug_from_env() if debug is None else bool(debug)
         self.params = make_params(batch=batch, seqlen_q=seqlen_q, num_heads=num_heads, num_pages=num_pages,
                                   max_blocks_per_seq=max_blocks_per_seq, kv_dtype=kv_dtype, causal=causal,
                                   softmax_scale=softmax_scale, num_workgroups=num_workgroups, fp8_path=fp8_path)
@@ -384,8 +414,35 @@ class MlaDecode:
         mla_get_workspace(self.params, seqlens.data_ptr(), self.workspace.data_ptr(), self.workspace_bytes,
                           self._stream())
 
+    def check_device_values(self, block_table, seqlens) -> None:
+        """The debug mode's synchronous checks (raises MlaDeviceError)."""
+        p = self.params
+        sl = seqlens.cpu()
+        lo, hi = p.seqlen_q, p.max_blocks_per_seq * PAGE_SIZE
+        bad = ((sl < lo) | (sl > hi)).nonzero().flatten().tolist()
+        if bad:
+            b = bad[0]
+            raise MlaDeviceError(f"seqlens[{b}] = {int(sl[b])} is outside [{lo}, {hi}]", MLA_FLAG_SEQLEN_CLAMPED)
+        bt = block_table.cpu()
+        for b in range(p.batch):
+            n = (int(sl[b]) + PAGE_SIZE - 1) // PAGE_SIZE
+            row = bt[b, :n]
+            out = ((row < 0) | (row >= p.num_pages)).nonzero().flatten().tolist()
+            if out:
+                j = out[0]
+                raise MlaDeviceError(f"block_table[{b}][{j}] = {int(row[j])} is outside [0, {p.num_pages})",
+                                     MLA_FLAG_BAD_BLOCK)
+
+    def raise_on_flags(self) -> None:
+        """Debug mode: raise MlaDeviceError if a kernel has set a workspace flag."""
+        f = self.flags()
+        if f:
+            raise MlaDeviceError(f"decode reported: {describe_flags(f)} (flags 0x{f:x})", f)
+
     def decode(self, q, kv_cache, block_table, seqlens, kv_scale=None) -> None:
         check_decode_inputs(self.params, self.device, q, kv_cache, block_table, seqlens, kv_scale)
+        if self.debug:
+            self.check_device_values(block_table, seqlens)
         mla_decode_fwd(self.params, q.data_ptr(), kv_cache.data_ptr(), 0 if kv_scale is None else kv_scale.data_ptr(),
                        block_table.data_ptr(), seqlens.data_ptr(), self.workspace.data_ptr(), self.workspace_bytes,
                        self.out.data_ptr(), self.lse.data_ptr(), self._stream())
@@ -399,6 +456,8 @@ class MlaDecode:
             self.plan(seqlens)
         self.decode(q, kv_cache, block_table, seqlens, kv_scale)
         self.combine()
+        if self.debug:
+            self.raise_on_flags()
         return self.out, self.lse
 
     def flags(self) -> int:

@@ -78,3 +78,16 @@ def test_fp8_mismatches_raise(what):
         kv = torch.zeros((p.num_pages, 64, 576), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         M.check_decode_inputs(p, "cpu", q, kv, bt, sl, ks)
+
+
+def test_debug_flag_text_and_environment(monkeypatch):
+    import mla_latent_kv_fwd_amd as M
+    assert M.describe_flags(0) == "none"
+    text = M.describe_flags(M.MLA_FLAG_SEQLEN_CLAMPED | M.MLA_FLAG_BAD_PLAN)
+    assert "clamped" in text and "plan" in text and "block-table" not in text
+    monkeypatch.setenv("MLA_DEBUG", "1")
+    assert M.debug_from_env()
+    monkeypatch.setenv("MLA_DEBUG", "0")
+    assert not M.debug_from_env()
+    monkeypatch.delenv("MLA_DEBUG")
+    assert not M.debug_from_env()
