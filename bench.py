@@ -353,6 +353,18 @@ def parity(M, W, out, lse, rows, ref_o, ref_l, bf16_tol=True):
             "lse_max_abs": lerr, "within_tolerance": bool(ok)}
 
 
+def input_digest(wl):
+    """sha256 over the workload's inputs as the kernels read them (q~, the cache, its scales, the block table and
+    the lengths), so two runs can be checked to have measured the same data."""
+    import hashlib
+    import numpy as np
+    h = hashlib.sha256()
+    for x in (wl.q, wl.cache, wl.kv_scale, wl.block_table, wl.seqlens):
+        if x is not None:
+            h.update(memoryview(np.ascontiguousarray(x)).cast("B"))
+    return h.hexdigest()[:16]
+
+
 def percentiles(xs):
     import numpy as np
     a = np.asarray(xs, dtype=np.float64)
@@ -468,6 +480,7 @@ def measure(torch, M, W, name, *, steps, warmup, warm_seconds, copies=0, block=1
     res = {
         "workload": name, "batch": wl.batch, "heads": wl.num_heads, "seqlen_q": wl.s_q, "causal": wl.causal,
         "seqlens_sum": int(wl.seqlens.sum()), "kv_dtype": wl.kv_dtype, "page": 64, "cache_copies": copies,
+        "input_sha256": input_digest(wl),
         "route": route if fp8 else "bf16",
         "steps": steps, "warmup_steps_total": warm_total, "ms_per_step": round(ms_per_step, 5),
         "step_ms": percentiles(blocks), "ms_per_step_with_plan": round(ms_per_step + plan_ms, 5),
