@@ -353,6 +353,38 @@ def parity(M, W, out, lse, rows, ref_o, ref_l, bf16_tol=True):
             "lse_max_abs": lerr, "within_tolerance": bool(ok)}
 
 
+GRAPH_STEPS = 10
+
+
+def graph_step_ms(torch, step, copies, steps):
+    """Average time per step when GRAPH_STEPS steps, cycling the cache copies, are captured into one HIP graph
+    and the graph is replayed until about `steps` steps have run (after two warm-up replays).  The library only
+    launches kernels (no allocation, memset or synchronisation), so the step can be captured."""
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(GRAPH_STEPS):
+            step(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for i in range(GRAPH_STEPS):
+            step(i)
+    reps = max(1, steps // GRAPH_STEPS)
+    for _ in range(2):
+        g.replay()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (reps * GRAPH_STEPS)
+    del g
+    return ms
+
+
 def input_digest(wl):
     """sha256 over the workload's inputs as the kernels read them (q~, the cache, its scales, the block table and
     the lengths), so two runs can be checked to have measured the same data."""
@@ -473,6 +505,7 @@ def measure(torch, M, W, name, *, steps, warmup, warm_seconds, copies=0, block=1
     e1.record(stream)
     torch.cuda.synchronize()
     warm1_ms = e0.elapsed_time(e1) / steps
+    graph_ms = graph_step_ms(torch, step, copies, steps)
 
     flops, kv_bytes, alg_bytes = workload_counts(wl.seqlens, wl.num_heads, wl.s_q, wl.causal, wl.kv_dtype)
     tflops = flops / (ms_per_step * 1e-3) / 1e12
@@ -493,6 +526,10 @@ def measure(torch, M, W, name, *, steps, warmup, warm_seconds, copies=0, block=1
         "warm_single_copy": {"ms_per_step": round(warm1_ms, 5),
                              "tflops": round(flops / (warm1_ms * 1e-3) / 1e12, 2),
                              "note": "one cache copy reused every step: partly served by the last-level cache"},
+        "graph_replay": {"ms_per_step": round(graph_ms, 5), "tflops": round(flops / (graph_ms * 1e-3) / 1e12, 2),
+                         "note": f"the same kernels launched from one HIP graph holding {GRAPH_STEPS} captured "
+                                 "steps (cycling the cache copies); reported beside the eager stream launches "
+                                 "that ms_per_step times"},
         "flags": flags,
     }
     if parity_rows:
@@ -542,7 +579,8 @@ def main():
         "kernel_ms": r["kernel_ms"],
         "kernel_timing": f"decode: {max(100, args.roofline_launches)} back-to-back launches between one HIP event "
                          "pair on its stream; plan, combine: 50 back-to-back launches each",
-        "roofline": r["roofline"], "warm_single_copy": r["warm_single_copy"], "flags": r["flags"],
+        "roofline": r["roofline"], "warm_single_copy": r["warm_single_copy"], "graph_replay": r["graph_replay"],
+        "flags": r["flags"],
     }
     if not args.no_cpu:
         cb, (rows, ro, rl) = cpu_baseline(wl, args.cpu_seconds)
