@@ -572,7 +572,7 @@ def main():
         "ms_per_step": r["ms_per_step"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "fp8_e4m3" if r.get("route") == "mfma" else "bf16", "data": "synthetic",
         "config": {k: r[k] for k in ("workload", "batch", "heads", "seqlen_q", "seqlens_sum", "kv_dtype", "page",
-                                     "cache_copies")},
+                                     "cache_copies", "input_sha256")},
         "step": "decode + combine of one layer; the plan runs once per model step (kernel_ms.plan)",
         "step_ms": r["step_ms"], "ms_per_step_with_plan": r["ms_per_step_with_plan"],
         "kv_gbps": r["kv_gbps"], "kv_frac_hbm": r["kv_frac_hbm"], "tflops_frac_mfma": r["tflops_frac_mfma"],
