@@ -423,15 +423,14 @@ class MlaDecode:
         if bad:
             b = bad[0]
             raise MlaDeviceError(f"seqlens[{b}] = {int(sl[b])} is outside [{lo}, {hi}]", MLA_FLAG_SEQLEN_CLAMPED)
+        import torch
         bt = block_table.cpu()
-        for b in range(p.batch):
-            n = (int(sl[b]) + PAGE_SIZE - 1) // PAGE_SIZE
-            row = bt[b, :n]
-            out = ((row < 0) | (row >= p.num_pages)).nonzero().flatten().tolist()
-            if out:
-                j = out[0]
-                raise MlaDeviceError(f"block_table[{b}][{j}] = {int(row[j])} is outside [0, {p.num_pages})",
-                                     MLA_FLAG_BAD_BLOCK)
+        used = torch.arange(p.max_blocks_per_seq)[None, :] < ((sl + PAGE_SIZE - 1) // PAGE_SIZE)[:, None]
+        bad = (used & ((bt < 0) | (bt >= p.num_pages))).nonzero()
+        if len(bad):
+            b, j = int(bad[0, 0]), int(bad[0, 1])
+            raise MlaDeviceError(f"block_table[{b}][{j}] = {int(bt[b, j])} is outside [0, {p.num_pages})",
+                                 MLA_FLAG_BAD_BLOCK)
 
     def raise_on_flags(self) -> None:
         """Debug mode: raise MlaDeviceError if a kernel has set a workspace flag."""

@@ -91,3 +91,26 @@ def test_debug_flag_text_and_environment(monkeypatch):
     assert not M.debug_from_env()
     monkeypatch.delenv("MLA_DEBUG")
     assert not M.debug_from_env()
+
+
+def test_debug_checks_of_lengths_and_used_pages():
+    """The debug mode's host-side checks (MlaDecode.check_device_values), run on CPU tensors."""
+    import torch
+    import mla_latent_kv_fwd_amd as M
+
+    class Holder:
+        params = M.make_params(batch=2, seqlen_q=1, num_heads=16, num_pages=4, max_blocks_per_seq=4)
+
+    check = lambda bt, sl: M.MlaDecode.check_device_values(Holder(), torch.tensor(bt, dtype=torch.int32),
+                                                           torch.tensor(sl, dtype=torch.int32))
+    good = [[1, 2, -1, -1], [3, 0, -1, -1]]
+    check(good, [100, 100])
+    check([[1, 2, -1, -7], [3, 0, -1, -1]], [100, 100])   # an entry past a request's pages is not read
+    with pytest.raises(M.MlaDeviceError) as e:
+        check([[1, 2, -1, -1], [3, 9, -1, -1]], [100, 100])
+    assert e.value.flags == M.MLA_FLAG_BAD_BLOCK and "block_table[1][1] = 9" in str(e.value)
+    with pytest.raises(M.MlaDeviceError) as e:
+        check(good, [100, 257])                             # beyond 4 pages of 64
+    assert e.value.flags == M.MLA_FLAG_SEQLEN_CLAMPED
+    with pytest.raises(M.MlaDeviceError):
+        check(good, [0, 100])                               # below seqlen_q
